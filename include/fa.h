@@ -1,0 +1,131 @@
+/*
+ * fa.h -- C ABI of libfa: fused exact attention on AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V
+ * (the attention formula of the bjdmk.com.cn FlashAttention page, section
+ * "性能引擎") in one fused kernel with an online softmax, and its exact
+ * gradients by recomputing P from the stored row logsumexp (recomputation:
+ * pwwt.cn page, section "3. 重计算"; keeping only the logsumexp: hotelren.com
+ * FlashAttention-2 walkthrough, section 3.1).  The causal variant masks keys
+ * j > query i (lower-triangular mask: bjdmk.com.cn page, section "实战集成").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *   library never allocates, frees or keeps a pointer after it returns.
+ * - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *   The library never synchronises; kernel faults surface at the caller's
+ *   next synchronisation, as usual in HIP.
+ * - Element type of q, k, v, o, dout, dq, dk, dv: `dtype` (FA_F16 or
+ *   FA_BF16).  lse and the workspace are fp32.
+ * - Tensor layout: logical [B, N, H, D] (batch, sequence, head, head_dim),
+ *   the flash_attn_func layout of the hotelren.com walkthrough, section 5.
+ *   Element strides (b, n, h) per tensor are given by the optional strides
+ *   struct; the d stride is always 1.  NULL strides mean contiguous
+ *   [B, N, H, D] for every tensor.  A packed qkv [B, N, 3, H, D] tensor
+ *   (bjdmk.com.cn page, section "实战集成") is passed as three views with
+ *   n-stride 3*H*D and h-stride D.
+ * - lse is fp32, contiguous [B, H, N]: LSE[b,h,i] = ln sum_j exp(scale*q_i.k_j)
+ *   over the unmasked keys j (natural logarithm of the scaled scores).
+ * - Sizes: B, H, N >= 1 (N_q = N_k = N); D in {64, 128}.
+ * - Return value: FA_OK or an error status.  Argument errors are detected
+ *   before any HIP call and leave every buffer untouched.  The functions
+ *   never print and never abort.
+ * - Stateless and reentrant; concurrent calls on different streams are safe
+ *   as long as their output and workspace buffers do not overlap.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, non-finite scale,
+                             causal not 0/1, unknown dtype, workspace too small */
+  FA_ERR_UNSUPPORTED = 2, /* D not 64/128, tensor pointer not 16-byte aligned
+                             (lse: 4-byte; workspace: 256-byte),
+                             b/n/h stride not a multiple of 8 elements, or a
+                             size whose element offsets overflow int64 */
+  FA_ERR_HIP = 3          /* a HIP runtime call failed (no device, launch error) */
+} fa_status;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Element strides of one logical [B, N, H, D] tensor (stride of d is 1). */
+typedef struct {
+  int64_t b, n, h;
+} fa_stride3;
+
+typedef struct {
+  fa_stride3 q, k, v, o;
+} fa_fwd_strides;
+
+typedef struct {
+  fa_stride3 q, k, v, o, dout, dq, dk, dv;
+} fa_bwd_strides;
+
+/*
+ * fa_fwd -- fused attention forward.
+ *   q, k, v : inputs, [B, N, H, D] (strided), dtype.
+ *   o       : output, [B, N, H, D] (strided), dtype; every element written.
+ *   lse     : output, fp32 contiguous [B, H, N]; every element written.
+ *   causal  : 0 = full attention, 1 = key j visible to query i iff j <= i.
+ *   scale   : multiplies q.k before the softmax; any finite value
+ *             (1/sqrt(D) is the formula's choice).
+ *   strides : NULL or the element strides of q, k, v, o.
+ * o must not alias q, k or v.  Extra device memory: none.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int D, int causal, float scale, int dtype,
+           const fa_fwd_strides* strides, hipStream_t stream);
+
+/*
+ * fa_bwd_workspace_bytes -- size of the fp32 scratch fa_bwd needs:
+ * the row vector Dvec = rowsum(dO o O) [B, H, N] and the dQ accumulator
+ * [B, H, N, D], each rounded up to 256 bytes.  O(N*D) per head; no N*N term.
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
+
+/*
+ * fa_bwd -- attention backward by recomputation.
+ *   q, k, v, o, lse : exactly as given to / produced by fa_fwd with the same
+ *                     B, H, N, D, causal, scale and dtype.
+ *   dout            : gradient of the loss w.r.t. o, [B, N, H, D], dtype.
+ *   dq, dk, dv      : outputs, [B, N, H, D] (strided), dtype; overwritten
+ *                     (not accumulated into).  They may be views into one
+ *                     packed dqkv tensor but must not overlap each other or
+ *                     any input.
+ *   workspace       : device buffer of at least
+ *                     fa_bwd_workspace_bytes(B, H, N, D) bytes, 256-byte
+ *                     aligned; contents undefined on entry and on exit.
+ * Three kernels are enqueued on `stream`: the Dvec preprocess (which also
+ * clears the dQ accumulator), the K/V-block-parallel dK/dV kernel that
+ * accumulates dQ with fp32 atomics, and the dQ conversion.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int D, int causal, float scale, int dtype,
+           const fa_bwd_strides* strides, void* workspace,
+           size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_str(int status);
+
+/* Library version string, e.g. "fa-gfx950 0.1.0" (static string). */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

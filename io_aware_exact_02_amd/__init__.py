@@ -1,0 +1,11 @@
+"""Fused exact attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in libfa.so (HIP kernels behind a C ABI, include/fa.h);
+this package is its thin Python binding.
+"""
+
+from .attention import (FaArgError, bwd, flash_attn_func, flash_attn_qkvpacked_func, fwd,
+                        workspace_bytes)
+
+__all__ = ["fwd", "bwd", "flash_attn_func", "flash_attn_qkvpacked_func", "workspace_bytes",
+           "FaArgError"]

@@ -1,0 +1,183 @@
+"""Python binding of libfa: fused exact attention on MI355X.
+
+Argument marshalling only.  torch supplies device memory and the current
+stream; every step of the computation runs in libfa's HIP kernels.  There
+is no fallback path: if libfa.so is missing the first call raises.
+
+API names follow the pages' usage: ``flash_attn_func(q, k, v, causal)`` on
+``[batch, seq, heads, head_dim]`` tensors (hotelren.com FlashAttention-2
+walkthrough, sections 4 and 5) and ``flash_attn_qkvpacked_func(qkv)`` on a
+packed ``[B, N, 3, H, D]`` tensor (bjdmk.com.cn page, section "实战集成").
+Inputs must be fp16 or bf16 -- fp32 is rejected, as the walkthrough's
+section 5 notes for the original library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
+
+
+class FaArgError(ValueError):
+    """An argument the library rejects (shape, dtype, device, layout)."""
+
+
+def _check_inputs(*tensors):
+    t0 = tensors[0]
+    if t0.dim() != 4:
+        raise FaArgError(f"expected [batch, seq, heads, head_dim] tensors, got {tuple(t0.shape)}")
+    if t0.dtype not in _DTYPES:
+        raise FaArgError(f"only float16 / bfloat16 inputs are supported, got {t0.dtype}")
+    for t in tensors[1:]:
+        if t.shape != t0.shape:
+            raise FaArgError(f"shape mismatch: {tuple(t.shape)} vs {tuple(t0.shape)}")
+        if t.dtype != t0.dtype:
+            raise FaArgError(f"dtype mismatch: {t.dtype} vs {t0.dtype}")
+        if t.device != t0.device:
+            raise FaArgError(f"device mismatch: {t.device} vs {t0.device}")
+    B, N, H, D = t0.shape
+    if D not in (64, 128):
+        raise FaArgError(f"head_dim must be 64 or 128, got {D}")
+    if t0.device.type != "cuda":
+        raise FaArgError(f"inputs must be on a GPU device, got {t0.device}")
+    return B, N, H, D
+
+
+def _usable(t: torch.Tensor) -> torch.Tensor:
+    """The kernels need d-stride 1, b/n/h strides that are multiples of 8
+    elements and a 16-byte aligned base; copy otherwise."""
+    s = t.stride()
+    if s[3] != 1 or any(x % 8 for x in s[:3]) or t.data_ptr() % 16:
+        return t.contiguous()
+    return t
+
+
+def _stride3(t: torch.Tensor) -> _lib.Stride3:
+    s = t.stride()
+    return _lib.Stride3(s[0], s[1], s[2])
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _scale(softmax_scale, D):
+    return 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+
+
+def _raise(status: int, what: str):
+    msg = _lib.load().fa_status_str(status).decode()
+    if status in (_lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED):
+        raise FaArgError(f"{what}: {msg}")
+    raise RuntimeError(f"{what}: {msg}")
+
+
+def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
+    """Forward pass.  Returns (o [B,N,H,D], lse [B,H,N] fp32)."""
+    lib = _lib.load()
+    B, N, H, D = _check_inputs(q, k, v)
+    q, k, v = _usable(q), _usable(k), _usable(v)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
+    else:
+        _check_inputs(q, out)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise FaArgError("lse must be a contiguous float32 [B, H, N] tensor")
+    st = _lib.FwdStrides(_stride3(q), _stride3(k), _stride3(v), _stride3(out))
+    status = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), B, H, N, D, int(bool(causal)),
+                        _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
+                        _stream(q))
+    if status != _lib.FA_OK:
+        _raise(status, "fa_fwd")
+    return out, lse
+
+
+def workspace_bytes(B: int, H: int, N: int, D: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, D))
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass.  Returns (dq, dk, dv), each [B,N,H,D] in the input type."""
+    lib = _lib.load()
+    B, N, H, D = _check_inputs(q, k, v, o, dout)
+    q, k, v, o, dout = (_usable(t) for t in (q, k, v, o, dout))
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise FaArgError("lse must be a contiguous float32 [B, H, N] tensor")
+    if dq is None:
+        dq = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
+    _check_inputs(q, dq, dk, dv)
+    need = lib.fa_bwd_workspace_bytes(B, H, N, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib.BwdStrides(*(_stride3(t) for t in (q, k, v, o, dout, dq, dk, dv)))
+    status = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                        dv.data_ptr(), B, H, N, D, int(bool(causal)),
+                        _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
+                        workspace.data_ptr(), workspace.numel(), _stream(q))
+    if status != _lib.FA_OK:
+        _raise(status, "fa_bwd")
+    return dq, dk, dv
+
+
+class _FlashAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, softmax_scale):
+        o, lse = fwd(q, k, v, causal, softmax_scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal = causal
+        ctx.softmax_scale = softmax_scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, _usable(dout), ctx.causal, ctx.softmax_scale)
+        return dq, dk, dv, None, None
+
+
+class _FlashAttnQKVPacked(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, qkv, causal, softmax_scale):
+        q, k, v = qkv.unbind(dim=2)
+        o, lse = fwd(q, k, v, causal, softmax_scale)
+        ctx.save_for_backward(qkv, o, lse)
+        ctx.causal = causal
+        ctx.softmax_scale = softmax_scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        qkv, o, lse = ctx.saved_tensors
+        q, k, v = qkv.unbind(dim=2)
+        dqkv = torch.empty_like(qkv)
+        dq, dk, dv = dqkv.unbind(dim=2)
+        bwd(q, k, v, o, lse, _usable(dout), ctx.causal, ctx.softmax_scale, dq=dq, dk=dk, dv=dv)
+        return dqkv, None, None
+
+
+def flash_attn_func(q, k, v, causal: bool = False, softmax_scale=None):
+    """Exact attention on [B, N, H, D] tensors, differentiable."""
+    return _FlashAttn.apply(q, k, v, causal, softmax_scale)
+
+
+def flash_attn_qkvpacked_func(qkv, causal: bool = False, softmax_scale=None):
+    """Exact attention on a packed [B, N, 3, H, D] tensor; returns [B, N, H, D].
+    The gradient lands in one packed dqkv tensor (no copies of q, k, v)."""
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise FaArgError(f"expected qkv of shape [B, N, 3, H, D], got {tuple(qkv.shape)}")
+    return _FlashAttnQKVPacked.apply(qkv, causal, softmax_scale)

@@ -1,0 +1,162 @@
+// Host side of libfa: argument validation and kernel launches behind the
+// C ABI declared in include/fa.h.  Every check runs before the first HIP
+// call, so an invalid call has no side effect and needs no device.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr int64_t kI64Max = INT64_MAX;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa::Strides contiguous(int N, int H, int D) {
+  return fa::Strides{static_cast<int64_t>(N) * H * D, static_cast<int64_t>(H) * D, D};
+}
+
+fa::Strides from_abi(const fa_stride3& s) { return fa::Strides{s.b, s.n, s.h}; }
+
+// Strides must keep 16-byte alignment of every row start and must address
+// only non-negative offsets that fit int64.
+int check_strides(const fa::Strides& s, int B, int N, int H, int D) {
+  if (s.b < 0 || s.n < 0 || s.h < 0) return FA_ERR_UNSUPPORTED;
+  if (s.b % 8 || s.n % 8 || s.h % 8) return FA_ERR_UNSUPPORTED;
+  // Largest element offset: (B-1)*sb + (N-1)*sn + (H-1)*sh + D-1.
+  const double bound = static_cast<double>(B - 1) * s.b + static_cast<double>(N - 1) * s.n +
+                       static_cast<double>(H - 1) * s.h + D;
+  if (bound >= 4.0e18) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_sizes(int B, int H, int N, int D, int causal, float scale, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  // Row index b*H*N + n and the flattened grid must fit 32 bits.
+  const int64_t rows = static_cast<int64_t>(B) * H * N;
+  if (rows > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
+  if (rows * D > kI64Max / 8) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int D, int causal, float scale, int dtype, const fa_fwd_strides* strides,
+           hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  fa::FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  if (strides) {
+    p.sq = from_abi(strides->q);
+    p.sk = from_abi(strides->k);
+    p.sv = from_abi(strides->v);
+    p.so = from_abi(strides->o);
+  } else {
+    p.sq = p.sk = p.sv = p.so = contiguous(N, H, D);
+  }
+  for (const fa::Strides* s : {&p.sq, &p.sk, &p.sv, &p.so}) {
+    st = check_strides(*s, B, N, H, D);
+    if (st != FA_OK) return st;
+  }
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  const float c = std::fabs(scale) * 1.4426950408889634f;
+  p.c = c > 1e-30f ? c : 1e-30f;
+  p.negate_q = scale < 0.0f ? 1 : 0;
+  const hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int D) {
+  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return 0;
+  const size_t rows = static_cast<size_t>(B) * H * N;
+  return align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+           int causal, float scale, int dtype, const fa_bwd_strides* strides, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, D)) return FA_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq),
+                          static_cast<const void*>(dk), static_cast<const void*>(dv)}) {
+    if (!aligned16(ptr)) return FA_ERR_UNSUPPORTED;
+  }
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_UNSUPPORTED;
+  fa::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  if (strides) {
+    p.sq = from_abi(strides->q);
+    p.sk = from_abi(strides->k);
+    p.sv = from_abi(strides->v);
+    p.so = from_abi(strides->o);
+    p.sdo = from_abi(strides->dout);
+    p.sdq = from_abi(strides->dq);
+    p.sdk = from_abi(strides->dk);
+    p.sdv = from_abi(strides->dv);
+  } else {
+    p.sq = p.sk = p.sv = p.so = p.sdo = p.sdq = p.sdk = p.sdv = contiguous(N, H, D);
+  }
+  for (const fa::Strides* s : {&p.sq, &p.sk, &p.sv, &p.so, &p.sdo, &p.sdq, &p.sdk, &p.sdv}) {
+    st = check_strides(*s, B, N, H, D);
+    if (st != FA_OK) return st;
+  }
+  const size_t rows = static_cast<size_t>(B) * H * N;
+  p.dvec = static_cast<float*>(workspace);
+  p.dq_accum = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(rows * sizeof(float)));
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_bwd(p, dtype, D, causal, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head dim, alignment or stride";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    default: return "unknown fa status";
+  }
+}
+
+const char* fa_version(void) { return "fa-gfx950 0.1.0"; }
+
+}  // extern "C"

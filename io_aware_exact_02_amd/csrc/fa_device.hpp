@@ -1,0 +1,128 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// operand vector types, the gfx950 MFMA wrappers, half-precision packing and
+// small LDS / global access helpers.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Element-type tags.  Storage is always 16-bit; the tag selects the MFMA
+// flavour and the fp32 -> half rounding (round-to-nearest-even for both).
+struct BF16 {
+  static constexpr bool is_bf16 = true;
+};
+struct F16 {
+  static constexpr bool is_bf16 = false;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// v_mfma_f32_32x32x16_{bf16,f16}: C[32x32] += A[32x16] * B[16x32].
+// Lane L holds A row (L % 32), B column (L % 32), each with the 8 k-values
+// 8*(L/32) .. 8*(L/32)+7 of the 16-wide k slice (the same k mapping for A
+// and B), and C column (L % 32), rows 8*(i/4) + 4*(L/32) + (i%4), i = 0..15.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b,
+                                               const f32x16& c) {
+  if constexpr (T::is_bf16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Two fp32 -> one packed pair of halves, round-to-nearest-even.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (T::is_bf16) {
+    bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    f16x2 v = __builtin_convertvector((f32x2){lo, hi}, f16x2);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ uint16_t to_half_bits(float x) {
+  return static_cast<uint16_t>(pack2<T>(x, 0.0f) & 0xffffu);
+}
+
+// Eight consecutive fp32 values -> one 16-byte MFMA operand.
+template <typename T>
+__device__ __forceinline__ u32x4 pack8(const float* v) {
+  return (u32x4){pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]),
+                 pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7])};
+}
+
+template <typename T>
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  if constexpr (T::is_bf16) {
+    return __uint_as_float(bits16 << 16);
+  } else {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+  }
+}
+
+// Dot product of two packed 8-half vectors in fp32 (used by the backward
+// preprocess; products are exact in fp32, sums round).
+template <typename T>
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b) {
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    s += half_bits_to_float<T>(a[w] & 0xffffu) * half_bits_to_float<T>(b[w] & 0xffffu);
+    s += half_bits_to_float<T>(a[w] >> 16) * half_bits_to_float<T>(b[w] >> 16);
+  }
+  return s;
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void stg16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void lds_write16(uint16_t* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Value of lane (L ^ 32): exchange between the two 32-lane halves.
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Permutation of the 32 rows of an MFMA A operand that makes the C layout of
+// the product give each lane 8 consecutive row indices per 16-row slice:
+// swaps bits 2 and 3 of the row index (an involution).  With A row m holding
+// item sigma(m), C value i of lane L is item 16*(i/8) + 8*(L/32) + (i%8).
+__device__ __forceinline__ int sigma32(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+__host__ __device__ constexpr int c_item(int i, int hh) {
+  return 16 * (i / 8) + 8 * hh + (i % 8);
+}
+// Row of C value i of lane half hh when A rows are in natural order.
+__host__ __device__ constexpr int c_row(int i, int hh) {
+  return 8 * (i / 4) + 4 * hh + (i % 4);
+}
+
+}  // namespace fa

@@ -1,0 +1,219 @@
+// Fused attention forward for gfx950.
+//
+// One kernel computes O = softmax(scale * Q K^T) V for a block of query rows
+// without ever writing S or P to memory: K/V tiles are staged through LDS,
+// both products run on the matrix cores, and the softmax is carried online
+// with a running row maximum m and normaliser l (the tiling / online-softmax
+// scheme of the pwwt.cn page, section "2. 分块处理").  The output accumulator
+// is kept unscaled and divided by l once at the end, and only the row
+// logsumexp is stored for the backward pass (hotelren.com FlashAttention-2
+// walkthrough, section 3.1; its printed recurrence is garbled, the form used
+// here is O~ <- diag(exp(m_old - m_new)) O~ + exp(S - m_new) V).
+// Parallelism runs over (batch, head, query block) as in section 3.2 of the
+// same walkthrough; causal tiles above the diagonal are skipped.
+//
+// Work split: a workgroup of 4 wave64s owns 128 query rows, 32 per wave.
+// Each wave computes S^T = K Q^T for its rows (K from LDS as the A operand,
+// its Q rows held in registers as the B operand), so the C layout of S^T
+// leaves one query row per lane -- the row max, the rescale factor and the
+// output rescale are then per-lane scalars.  K rows are stored in LDS under
+// the sigma32 row permutation so that the P values a lane holds are exactly
+// the B operand of the next product O^T += V^T P^T, with no data movement.
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int NW = 4;        // waves per workgroup
+  static constexpr int BR = 32 * NW;  // query rows per workgroup
+  static constexpr int BC = 64;       // keys per K/V tile
+  static constexpr int KP = D + 8;    // K tile row pitch (elements)
+  static constexpr int VP = BC + 8;   // V^T tile row pitch (elements)
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+  using Cfg = FwdCfg<D>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, KP = Cfg::KP, VP = Cfg::VP;
+  constexpr int KC = D / 16;   // 16-wide k slices of Q K^T
+  constexpr int NB = BC / 32;  // 32-key blocks per tile
+  constexpr int DB = D / 32;   // 32-wide d blocks of O
+  constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
+  constexpr int NCH = BC * CPR / 256;
+  static_assert(NCH * 256 == BC * CPR, "tile load must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = p.B * p.H;
+  const int bh = blockIdx.x % BH;
+  const int qblk = p.num_qblocks - 1 - static_cast<int>(blockIdx.x / BH);
+  const int b = bh / p.H;
+  const int h = bh % p.H;
+  const int N = p.N;
+
+  const uint16_t* qbase = p.q + b * p.sq.b + h * p.sq.h;
+  const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
+  const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
+
+  const int q0 = qblk * BR + wave * 32;  // first query row of this wave
+  const int qrow = q0 + l32;             // the query row this lane serves
+
+  // B operand of S^T = K Q^T: q[qrow][16*kc + 8*hh + 0..7].
+  u32x4 qreg[KC];
+  const uint32_t sign = p.negate_q ? 0x80008000u : 0u;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qrow < N) v = ldg16(qbase + static_cast<int64_t>(qrow) * p.sq.n + 16 * kc + 8 * hh);
+    qreg[kc] = v ^ sign;
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
+  float m = -INFINITY;  // running max of scale*log2(e)*s over this row
+  float l = 0.0f;       // running sum of exp2(t - m), this lane's keys only
+
+  const int qlast = min(qblk * BR + BR, N) - 1;
+  const int ntiles = CAUSAL ? (qlast / BC + 1) : ((N + BC - 1) / BC);
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * BC;
+    __syncthreads();  // previous tile fully consumed
+#pragma unroll
+    for (int it = 0; it < NCH; ++it) {
+      const int c = tid + 256 * it;
+      const int row = c / CPR;
+      const int col = (c % CPR) * 8;
+      const int key = kv0 + row;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < N) {
+        kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + col);
+        vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + col);
+      }
+      const int lrow = (row & ~31) | sigma32(row & 31);
+      lds_write16(&Ks[lrow * KP + col], kv);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        Vt[(col + 2 * w) * VP + row] = static_cast<uint16_t>(vv[w] & 0xffffu);
+        Vt[(col + 2 * w + 1) * VP + row] = static_cast<uint16_t>(vv[w] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T blocks: C value i of lane (l32, hh) is the score of query qrow
+    // against key kv0 + 32*nb + c_item(i, hh).
+    f32x16 sacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      sacc[nb] = (f32x16){};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4 a = lds_read16(&Ks[(32 * nb + l32) * KP + 16 * kc + 8 * hh]);
+        sacc[nb] = mfma32x32x16<T>(a, qreg[kc], sacc[nb]);
+      }
+    }
+
+    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
+    if (need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + 32 * nb + c_item(i, hh);
+          if (key >= N || (CAUSAL && key > qrow)) sacc[nb][i] = -INFINITY;
+        }
+      }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(m, mx * p.c);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+
+    float rs = 0.0f;
+    u32x4 pb[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], p.c, -mnew));
+        rs += pv[i];
+      }
+      pb[nb][0] = pack8<T>(pv);
+      pb[nb][1] = pack8<T>(pv + 8);
+    }
+    l = l * alpha + rs;
+    m = mnew;
+
+    // O^T += V^T P^T: A = V^T rows (d) from LDS, B = this lane's P values.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      oacc[db] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const u32x4 a = lds_read16(&Vt[(32 * db + l32) * VP + 32 * nb + 16 * cc + 8 * hh]);
+          oacc[db] = mfma32x32x16<T>(a, pb[nb][cc], oacc[db]);
+        }
+      }
+    }
+  }
+
+  // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
+  const float lt = l + xor32(l);
+  const float inv = __builtin_amdgcn_rcpf(lt);
+  if (qrow < N) {
+    uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        const u32x2 v = {pack2<T>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                         pack2<T>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d) = v;
+      }
+    }
+    if (hh == 0) {
+      p.lse[static_cast<int64_t>(bh) * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+    }
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdParams& p_in, hipStream_t s) {
+  FwdParams p = p_in;
+  p.num_qblocks = (p.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
+  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_qblocks;
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s) {
+  if (dtype == 1) {
+    if (D == 64) return causal ? launch_fwd_t<BF16, 64, true>(p, s) : launch_fwd_t<BF16, 64, false>(p, s);
+    return causal ? launch_fwd_t<BF16, 128, true>(p, s) : launch_fwd_t<BF16, 128, false>(p, s);
+  }
+  if (D == 64) return causal ? launch_fwd_t<F16, 64, true>(p, s) : launch_fwd_t<F16, 64, false>(p, s);
+  return causal ? launch_fwd_t<F16, 128, true>(p, s) : launch_fwd_t<F16, 128, false>(p, s);
+}
+
+}  // namespace fa

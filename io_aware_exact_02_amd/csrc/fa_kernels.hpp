@@ -1,0 +1,49 @@
+// Kernel parameter blocks and host-side launchers (internal to libfa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct Strides {
+  int64_t b, n, h;  // element strides of a logical [B, N, H, D] tensor
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // [B, H, N] fp32
+  Strides sq, sk, sv, so;
+  int B, H, N;
+  int num_qblocks;  // ceil(N / rows per workgroup)
+  float c;          // |scale| * log2(e), at least 1e-30
+  int negate_q;     // 1 when scale < 0: q enters the scores negated
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;  // [B, H, N]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dvec;      // workspace: [B, H, N]
+  float* dq_accum;  // workspace: [B, H, N, D]
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  int B, H, N;
+  int num_kblocks;  // ceil(N / keys per workgroup)
+  float scale;
+  float c;  // scale * log2(e)
+};
+
+// dtype: 0 = f16, 1 = bf16.  Return the launch status.
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, hipStream_t s);
+
+}  // namespace fa

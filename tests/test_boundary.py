@@ -1,0 +1,141 @@
+"""CPU-side checks of the C ABI and the Python binding (no GPU needed).
+
+The library must load, export every function include/fa.h declares, and
+reject invalid arguments before making any HIP call.  Only argument-error
+paths are exercised here; nothing is launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from io_aware_exact_02_amd import _lib
+from io_aware_exact_02_amd import attention as fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libfa.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.fa_version().decode().startswith("fa-gfx950")
+    for st in range(4):
+        assert lib.fa_status_str(st)
+    assert b"unknown" in lib.fa_status_str(99)
+
+
+def test_workspace_bytes_is_linear_in_n():
+    lib = _lib.load()
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for (B, H, N, D) in [(1, 1, 1, 64), (2, 12, 2048, 64), (1, 16, 16384, 64), (1, 8, 8192, 128)]:
+        rows = B * H * N
+        assert lib.fa_bwd_workspace_bytes(B, H, N, D) == a256(4 * rows) + a256(4 * rows * D)
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
+
+
+# Fake device pointers: never dereferenced because validation fails first.
+P = 0x10000
+ARGS_OK = dict(B=1, H=1, N=128, D=64, causal=0, scale=0.125, dtype=_lib.FA_BF16)
+
+
+def _fwd(q=P, k=P, v=P, o=P, lse=P, strides=None, **kw):
+    a = dict(ARGS_OK, **kw)
+    st = ctypes.byref(strides) if strides is not None else None
+    return _lib.load().fa_fwd(q, k, v, o, lse, a["B"], a["H"], a["N"], a["D"], a["causal"],
+                              a["scale"], a["dtype"], st, None)
+
+
+def _bwd(ptrs=None, ws=P, ws_bytes=1 << 40, strides=None, **kw):
+    a = dict(ARGS_OK, **kw)
+    p = [P] * 9 if ptrs is None else ptrs
+    st = ctypes.byref(strides) if strides is not None else None
+    return _lib.load().fa_bwd(*p, a["B"], a["H"], a["N"], a["D"], a["causal"], a["scale"],
+                              a["dtype"], st, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(lse=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(B=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(H=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(N=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(causal=2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), _lib.FA_ERR_INVALID_ARG),
+    (dict(D=32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(D=256), _lib.FA_ERR_UNSUPPORTED),
+    (dict(q=P + 8), _lib.FA_ERR_UNSUPPORTED),
+    (dict(o=P + 2), _lib.FA_ERR_UNSUPPORTED),
+    (dict(lse=P + 2), _lib.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 12, N=1 << 12), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_before_launch(kw, expect):
+    assert _fwd(**kw) == expect
+
+
+def test_fwd_rejects_bad_strides():
+    good = _lib.Stride3(128 * 64, 64, 64)
+    for bad in (_lib.Stride3(128 * 64, 60, 64), _lib.Stride3(-8, 64, 64),
+                _lib.Stride3(128 * 64, 64, 4)):
+        for field in ("q", "k", "v", "o"):
+            s = _lib.FwdStrides(good, good, good, good)
+            setattr(s, field, bad)
+            assert _fwd(strides=s) == _lib.FA_ERR_UNSUPPORTED, (field, bad.n, bad.h)
+
+
+def test_bwd_rejects_before_launch():
+    need = _lib.load().fa_bwd_workspace_bytes(1, 1, 128, 64)
+    assert _bwd(ws_bytes=need - 1) == _lib.FA_ERR_INVALID_ARG
+    assert _bwd(ws=None) == _lib.FA_ERR_INVALID_ARG
+    assert _bwd(ws=P + 16) == _lib.FA_ERR_UNSUPPORTED       # workspace needs 256 B alignment
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = None
+        assert _bwd(ptrs=ptrs) == _lib.FA_ERR_INVALID_ARG, i
+    ptrs = [P] * 9
+    ptrs[6] = P + 4                                           # dq misaligned
+    assert _bwd(ptrs=ptrs) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd(D=80) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd(causal=-1) == _lib.FA_ERR_INVALID_ARG
+    good = _lib.Stride3(128 * 64, 64, 64)
+    s = _lib.BwdStrides(*([good] * 8))
+    s.dk = _lib.Stride3(128 * 64, 68, 64)
+    assert _bwd(strides=s) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_bad_inputs_without_gpu():
+    q = torch.zeros(1, 16, 2, 64, dtype=torch.float32)
+    with pytest.raises(fa.FaArgError, match="float16 / bfloat16"):
+        fa.fwd(q, q, q)
+    qb = q.to(torch.bfloat16)
+    with pytest.raises(fa.FaArgError, match="GPU"):
+        fa.fwd(qb, qb, qb)
+    with pytest.raises(fa.FaArgError, match="head_dim"):
+        x = torch.zeros(1, 16, 2, 32, dtype=torch.bfloat16)
+        fa._check_inputs(x, x, x)
+    with pytest.raises(fa.FaArgError, match=r"\[B, N, 3, H, D\]"):
+        fa.flash_attn_qkvpacked_func(torch.zeros(1, 16, 2, 2, 64, dtype=torch.float16))

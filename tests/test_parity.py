@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI via the Python binding)
+against the fp64 CPU oracle, element by element on the same seeded inputs.
+
+Tolerances: O max-abs <= 1e-2, LSE max-abs <= 1e-3, and each of dQ, dK, dV
+max-abs <= 5e-2 * max|reference|.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_02_amd as fa
+from oracle import attention as oa
+from workloads import WORKLOADS, make_inputs, random_qkv, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-2
+LSE_TOL = 1e-3
+G_TOL = 5e-2
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_forward_backward(inp, causal, scale=None, packed=False, dout=True):
+    """Run fa.fwd / fa.bwd on the device copies of ``inp``; returns numpy fp64."""
+    dev = torch.device("cuda")
+    if packed:
+        qkv = inp["qkv"].to(dev)
+        q, k, v = qkv.unbind(dim=2)
+    else:
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal, softmax_scale=scale)
+    out = {"O": o, "LSE": lse}
+    if dout:
+        do = inp["do"].to(dev)
+        if packed:
+            dqkv = torch.empty_like(qkv)
+            dq, dk, dv = dqkv.unbind(dim=2)
+            fa.bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=scale,
+                   dq=dq, dk=dk, dv=dv)
+        else:
+            dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=scale)
+        out.update(dQ=dq, dK=dk, dV=dv)
+    torch.cuda.synchronize()
+    return {key: t.detach().to("cpu", torch.float64).numpy() for key, t in out.items()}
+
+
+def assert_forward(got, O, LSE, what=""):
+    eo = np.max(np.abs(got["O"] - O)) if O.size else 0.0
+    el = np.max(np.abs(got["LSE"] - LSE)) if LSE.size else 0.0
+    assert np.all(np.isfinite(got["O"])) and np.all(np.isfinite(got["LSE"])), what
+    assert eo <= O_TOL, f"{what} O max-abs {eo:.3e}"
+    assert el <= LSE_TOL, f"{what} LSE max-abs {el:.3e}"
+    return eo, el
+
+
+def assert_grad(name, got, ref, what=""):
+    assert np.all(np.isfinite(got)), f"{what} {name} not finite"
+    mag = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref))
+    bound = G_TOL * mag if mag > 0 else 1e-3
+    assert err <= bound, f"{what} {name} max-abs {err:.3e} > {bound:.3e} (max|ref| {mag:.3e})"
+    return err / mag if mag > 0 else err
+
+
+def check_full(inp, causal, scale=None, packed=False, what=""):
+    got = gpu_forward_backward(inp, causal, scale, packed)
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=causal, scale=scale)
+    assert_forward(got, O, LSE, what)
+    dQ, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"],
+                                       causal=causal, scale=scale)
+    for name, ref in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        assert_grad(name, got[name], ref, what)
+
+
+# ------------------------------------------------------------ small shapes
+
+SMALL_N = [1, 2, 3, 17, 64, 127, 128, 129, 255, 300]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_small_shapes(N, D, causal, dtype):
+    what = f"N={N} D={D} causal={causal} {dtype}"
+    _say("case", what)
+    inp = random_qkv(2, N, 3, D, dtype, seed=7000 + N + D)
+    check_full(inp, causal, what=what)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_values(scale, causal):
+    """scale = 0 (uniform attention), a negative scale and a sharp one."""
+    what = f"scale={scale} causal={causal}"
+    _say("case", what)
+    inp = random_qkv(1, 200, 2, 64, "bf16", seed=7100)
+    check_full(inp, causal, scale=scale, what=what)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_strided_bhnd_input(D):
+    """A [B,H,N,D] tensor passed through a transposed view (strides only)."""
+    _say("case strided", D)
+    inp = random_qkv(2, 160, 4, D, "f16", seed=7200)
+    # Build [B,H,N,D] storage and hand the kernels its [B,N,H,D] view.
+    for name in ("q", "k", "v", "do"):
+        inp[name] = inp[name].transpose(1, 2).contiguous().transpose(1, 2)
+    check_full(inp, True, what=f"strided D={D}")
+
+
+# ------------------------------------------------------------ the five configs
+
+def test_config_c1():
+    w = WORKLOADS["c1"]
+    _say("case", w.describe())
+    check_full(make_inputs(w), w.causal, what="c1")
+
+
+def test_config_c2_packed():
+    w = WORKLOADS["c2"]
+    _say("case", w.describe())
+    check_full(make_inputs(w), w.causal, packed=True, what="c2")
+
+
+def test_config_c2_autograd_sum_loss():
+    """The qkv-packed usage with loss = out.sum() (dO = 1), through autograd."""
+    w = WORKLOADS["c2"]
+    _say("case c2 autograd out.sum()")
+    inp = make_inputs(w, dout="ones")
+    qkv = inp["qkv"].to("cuda").requires_grad_(True)
+    out = fa.flash_attn_qkvpacked_func(qkv)
+    assert out.shape == (w.B, w.N, w.H, w.D)
+    out.sum().backward()
+    assert qkv.grad is not None and qkv.grad.shape == qkv.shape
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"])
+    assert np.max(np.abs(out.detach().double().cpu().numpy() - O)) <= O_TOL
+    g = qkv.grad.double().cpu().numpy()
+    dQ, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"])
+    for idx, (name, ref) in enumerate((("dQ", dQ), ("dK", dK), ("dV", dV))):
+        assert_grad(name, g[:, :, idx], ref, "c2 autograd")
+
+
+def test_config_c3_packed():
+    w = WORKLOADS["c3"]
+    _say("case", w.describe())
+    check_full(make_inputs(w), w.causal, packed=True, what="c3")
+
+
+def test_config_c4_full():
+    """c4 in full: O, LSE, dQ, dK, dV of every head against the row-chunked
+    oracle."""
+    w = WORKLOADS["c4"]
+    _say("case", w.describe())
+    inp = make_inputs(w)
+    got = gpu_forward_backward(inp, w.causal)
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=True)
+    assert_forward(got, O, LSE, "c4")
+    dQ, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=True)
+    for name, ref in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        assert_grad(name, got[name], ref, "c4")
+
+
+def test_config_c5_sampled():
+    """c5: O, LSE, dQ at 256 sampled query rows of all 16 heads (row-local,
+    exact), dK and dV in full on heads 0 and 15."""
+    w = WORKLOADS["c5"]
+    _say("case", w.describe())
+    inp = make_inputs(w)
+    got = gpu_forward_backward(inp, w.causal)
+    rows = sample_rows(w.N, 256, seed=w.seed)
+    for h in range(w.H):
+        r = oa.attention_rows(inp["q"], inp["k"], inp["v"], inp["do"], 0, h, rows, causal=True)
+        sub = {"O": got["O"][0, rows, h], "LSE": got["LSE"][0, h, rows]}
+        assert_forward(sub, r["O"], r["LSE"], f"c5 head {h}")
+        # dQ rows: the tolerance scale is the max over the sampled rows
+        assert_grad("dQ", got["dQ"][0, rows, h], r["dQ"], f"c5 head {h}")
+    heads = [(0, 0), (0, w.H - 1)]
+    _, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=True,
+                                      heads=heads)
+    for (b, h) in heads:
+        assert_grad("dK", got["dK"][b, :, h], dK[b, :, h], f"c5 head {h}")
+        assert_grad("dV", got["dV"][b, :, h], dV[b, :, h], f"c5 head {h}")
+
+
+# ------------------------------------------------------------ properties
+
+def test_determinism():
+    """O, LSE, dK and dV are bitwise reproducible (dQ uses atomics)."""
+    w = WORKLOADS["c3"]
+    _say("case determinism c3")
+    inp = make_inputs(w)
+    a = gpu_forward_backward(inp, w.causal, packed=True)
+    b = gpu_forward_backward(inp, w.causal, packed=True)
+    for key in ("O", "LSE", "dK", "dV"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.max(np.abs(a["dQ"] - b["dQ"])) <= 1e-2 * np.max(np.abs(a["dQ"]))
+
+
+def test_gradient_sum_identities_on_gpu():
+    """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i hold for the GPU result."""
+    _say("case gradient sums")
+    inp = random_qkv(2, 1024, 4, 64, "bf16", seed=7300)
+    for causal in (False, True):
+        got = gpu_forward_backward(inp, causal)
+        # Rounding errors of the N terms add up like a random walk; 1e-2 of
+        # the sum of magnitudes leaves a wide margin over that.
+        dK_sum = got["dK"].sum(axis=1)
+        dV_sum = got["dV"].sum(axis=1)
+        do_sum = inp["do"].double().numpy().sum(axis=1)
+        assert np.all(np.abs(dK_sum) <= 1e-2 * np.abs(got["dK"]).sum(axis=1))
+        assert np.all(np.abs(dV_sum - do_sum) <= 1e-2 * np.abs(got["dV"]).sum(axis=1))
+
+
+def test_no_quadratic_memory():
+    """Fused forward + backward at N = 16384 allocates O(N*D) extra memory:
+    nothing near one N x N matrix (8.6 GB at this size)."""
+    w = WORKLOADS["c5"]
+    _say("case memory c5")
+    dev = torch.device("cuda")
+    inp = make_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    extra = torch.cuda.max_memory_allocated() - base
+    tensor = q.numel() * q.element_size()
+    allowed = 4 * tensor + lse.numel() * 4 + fa.workspace_bytes(w.B, w.H, w.N, w.D) + (1 << 20)
+    nn = w.B * w.H * w.N * w.N * 2
+    _say(f"extra {extra / 1e6:.1f} MB, allowed {allowed / 1e6:.1f} MB, one S matrix {nn / 1e9:.1f} GB")
+    assert extra <= allowed
