@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+Metric: attention forward + backward throughput in TFLOP/s (and as a
+fraction of the dense bf16/fp16 MFMA peak) over the sequence-length sweep
+N = 512 .. 16384.  One step runs fa_fwd and the three backward kernels once
+for each of the four workloads
+
+    c2  B=2  H=12 N=512   D=64  fp16 packed qkv, non-causal
+    c3  B=2  H=12 N=2048  D=64  fp16 packed qkv, non-causal
+    c4  B=1  H=8  N=8192  D=128 bf16 [B,N,H,D],  causal
+    c5  B=1  H=16 N=16384 D=64  bf16 [B,N,H,D],  causal
+
+with seeded N(0,1) inputs already resident in HBM.  FLOPs follow the usual
+convention: forward 4*B*H*N^2*D, backward 2.5x that (five products against
+two), both halved for causal masking.
+
+Prints ONE JSON line.  Besides the headline value it carries
+  roofline     : the dominant kernel (the dK/dV backward kernel at c5) timed
+                 with HIP events on its own stream inside the timed region,
+                 against the 2516.6 TFLOP/s dense MFMA peak;
+  cpu_baseline : the fp64 CPU oracle timed on a bounded sample (c3 heads);
+  per_config   : forward / backward times and TFLOP/s per workload;
+  memory_c3    : peak device memory of fused fwd+bwd vs an unfused S/P
+                 PyTorch baseline at c3 (untimed pass).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6  # MI355X dense bf16/fp16: 256 CU x 2.4 GHz x 4096 FLOP/clk
+METRIC = "attention fwd+bwd TFLOPs/s and % of MFMA bf16 peak, N=512..16K, 1 GPU"
+SWEEP = ("c2", "c3", "c4", "c5")
+DOMINANT = "c5"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_dkdv_c5.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_02_amd", "csrc", f)
+                  for f in ("fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp")]
+
+
+def conv_flops(w):
+    f = 4.0 * w.B * w.H * w.N * w.N * w.D
+    if w.causal:
+        f /= 2
+    return f, 2.5 * f
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None if absent or taken on different kernel code."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 oracle (as it stands) on whole heads of c3 until the budget is
+    used; TFLOP/s under the same convention as the GPU figure."""
+    from oracle import attention as oa
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["c3"]
+    inp = make_inputs(w)
+    fwd_f, bwd_f = conv_flops(w)
+    per_head = (fwd_f + bwd_f) / (w.B * w.H)
+    done, t0 = 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = slice(h, h + 1)
+            q, k, v, do = (inp[n][b:b + 1, :, sl] for n in ("q", "k", "v", "do"))
+            oa.attention_forward(q, k, v, causal=w.causal)
+            oa.attention_backward(q, k, v, do, causal=w.causal)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done * per_head / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, fwd+bwd of {done} of the {w.B * w.H} heads of c3 "
+                      f"({w.describe()}) in {dt:.1f} s"}
+
+
+def unfused_memory_c3(torch, fa, w, inp):
+    """Peak device memory of fused fwd+bwd vs the unfused three-step path
+    (S = QK^T, P = softmax(S), O = PV, with S and P materialised) at c3."""
+    dev = torch.device("cuda")
+    qkv = inp["qkv"].to(dev)
+    do = inp["do"].to(dev)
+    torch.cuda.synchronize()
+    res = {}
+    # fused
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    q, k, v = qkv.unbind(dim=2)
+    o, lse = fa.fwd(q, k, v, causal=False)
+    dqkv = torch.empty_like(qkv)
+    fa.bwd(q, k, v, o, lse, do, dq=dqkv[:, :, 0], dk=dqkv[:, :, 1], dv=dqkv[:, :, 2])
+    torch.cuda.synchronize()
+    res["fused_peak_bytes"] = torch.cuda.max_memory_allocated() - base
+    del o, lse, dqkv
+    # unfused: explicit products, contiguous operands only
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    scale = 1.0 / (w.D ** 0.5)
+    qh, kh, vh = (t.permute(0, 2, 1, 3).contiguous() for t in qkv.unbind(dim=2))
+    doh = do.permute(0, 2, 1, 3).contiguous()
+    S = torch.matmul(qh, kh.transpose(-1, -2).contiguous()) * scale
+    P = torch.softmax(S.float(), dim=-1).to(qkv.dtype)
+    O = torch.matmul(P, vh)
+    dV = torch.matmul(P.transpose(-1, -2).contiguous(), doh)
+    dP = torch.matmul(doh, vh.transpose(-1, -2).contiguous())
+    Dv = (doh.float() * O.float()).sum(-1, keepdim=True)
+    dS = (P.float() * (dP.float() - Dv)).to(qkv.dtype)
+    dQ = torch.matmul(dS, kh) * scale
+    dK = torch.matmul(dS.transpose(-1, -2).contiguous(), qh) * scale
+    torch.cuda.synchronize()
+    res["unfused_peak_bytes"] = torch.cuda.max_memory_allocated() - base
+    del S, P, O, dV, dP, Dv, dS, dQ, dK
+    res["ratio"] = round(res["unfused_peak_bytes"] / max(res["fused_peak_bytes"], 1), 2)
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default=",".join(SWEEP))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-memory", action="store_true", help="skip the c3 memory comparison")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention hot path here has no "
+              "multi-GPU mode (heads shard across GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import io_aware_exact_02_amd as fa
+    from workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    names = [n.strip() for n in args.workloads.split(",") if n.strip()]
+    cases = []
+    for name in names:
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        c = {"w": w, "inp": inp}
+        if w.layout == "packed":
+            qkv = inp["qkv"].to(dev)
+            c["q"], c["k"], c["v"] = qkv.unbind(dim=2)
+            dqkv = torch.empty_like(qkv)
+            c["dq"], c["dk"], c["dv"] = dqkv.unbind(dim=2)
+            c["keep"] = (qkv, dqkv)
+        else:
+            c["q"], c["k"], c["v"] = (inp[n].to(dev) for n in ("q", "k", "v"))
+            c["dq"], c["dk"], c["dv"] = (torch.empty_like(c["q"]) for _ in range(3))
+        c["do"] = inp["do"].to(dev)
+        c["o"] = torch.empty((w.B, w.N, w.H, w.D), dtype=w.torch_dtype, device=dev)
+        c["lse"] = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        c["ws"] = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.D), dtype=torch.uint8,
+                              device=dev)
+        c["fwd_f"], c["bwd_f"] = conv_flops(w)
+        c["ev"] = []
+        cases.append(c)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(record):
+        for c in cases:
+            evs = {}
+            if record:
+                for key in ("f0", "f1", "k0", "k1", "b1"):
+                    evs[key] = torch.cuda.Event(enable_timing=True)
+                evs["f0"].record(stream)
+            fa.fwd(c["q"], c["k"], c["v"], causal=c["w"].causal, out=c["o"], lse=c["lse"])
+            if record:
+                evs["f1"].record(stream)
+            hook = (lambda tag, e=evs: e["k0" if tag == "dkdv_begin" else "k1"].record(stream)) \
+                if record else None
+            fa.bwd(c["q"], c["k"], c["v"], c["o"], c["lse"], c["do"], causal=c["w"].causal,
+                   dq=c["dq"], dk=c["dk"], dv=c["dv"], workspace=c["ws"], stage_hook=hook)
+            if record:
+                evs["b1"].record(stream)
+                c["ev"].append(evs)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    flops_step = sum(c["fwd_f"] + c["bwd_f"] for c in cases)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    per_config = {}
+    for c in cases:
+        w = c["w"]
+        fwd_ms = sum(e["f0"].elapsed_time(e["f1"]) for e in c["ev"]) / len(c["ev"])
+        bwd_ms = sum(e["f1"].elapsed_time(e["b1"]) for e in c["ev"]) / len(c["ev"])
+        dkdv_ms = sum(e["k0"].elapsed_time(e["k1"]) for e in c["ev"]) / len(c["ev"])
+        per_config[w.name] = {
+            "shape": w.describe(),
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "bwd_dkdv_kernel_ms": round(dkdv_ms, 4),
+            "fwd_tflops": round(c["fwd_f"] / fwd_ms / 1e9, 2),
+            "bwd_tflops": round(c["bwd_f"] / bwd_ms / 1e9, 2),
+            "fwd_pct_peak": round(100 * c["fwd_f"] / fwd_ms / 1e9 / PEAK_MFMA_TFLOPS, 2),
+            "bwd_pct_peak": round(100 * c["bwd_f"] / bwd_ms / 1e9 / PEAK_MFMA_TFLOPS, 2),
+        }
+
+    roofline = None
+    dom = next((c for c in cases if c["w"].name == DOMINANT), None)
+    if dom is not None:
+        dkdv_ms = per_config[DOMINANT]["bwd_dkdv_kernel_ms"]
+        achieved = dom["bwd_f"] / dkdv_ms / 1e9
+        roofline = {"bound": "mfma", "kernel": "bwd_dkdv_kernel",
+                    "workload": dom["w"].describe(),
+                    "flops_per_launch": dom["bwd_f"],
+                    "avg_launch_ms": dkdv_ms,
+                    "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                    "traffic": traffic_record()}
+
+    memory = None
+    if not args.no_memory and "c3" in names:
+        c3 = next(c for c in cases if c["w"].name == "c3")
+        memory = unfused_memory_c3(torch, fa, c3["w"], c3["inp"])
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    dtypes = sorted({c["w"].dtype for c in cases})
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "wall_s_timed": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "+".join(dtypes) + " (fp32 accumulate)",
+        "data": "synthetic: seeded N(0,1) q, k, v, dO",
+        "config": {"workload": "attention fwd+bwd sweep " + ", ".join(
+            f"{c['w'].name}: {c['w'].describe()}" for c in cases),
+            "flops_per_step": flops_step},
+        "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+        "memory_c3": memory,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -118,6 +118,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const fa_bwd_strides* strides, void* workspace,
            size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fa_bwd_stages -- fa_bwd split into its three kernels, for callers that
+ * schedule or time them separately.  Arguments are those of fa_bwd; `stages`
+ * is a bit mask: FA_STAGE_PREPROCESS (Dvec and the cleared dQ accumulator,
+ * written to the workspace), FA_STAGE_DKDV (dK, dV, and dQ accumulated in
+ * the workspace) and FA_STAGE_DQ (dq from the accumulator).  Each stage
+ * reads what the previous one left in the same workspace, so the stages must
+ * run in this order on one stream with the same workspace; fa_bwd is
+ * fa_bwd_stages with all three bits.  stages = 0 or unknown bits:
+ * FA_ERR_INVALID_ARG.
+ */
+#define FA_STAGE_PREPROCESS 1u
+#define FA_STAGE_DKDV 2u
+#define FA_STAGE_DQ 4u
+#define FA_STAGE_ALL 7u
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk,
+                  void* dv, int B, int H, int N, int D, int causal,
+                  float scale, int dtype, const fa_bwd_strides* strides,
+                  void* workspace, size_t workspace_bytes, unsigned stages,
+                  hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(int status);
 

@@ -16,7 +16,9 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F16, FA_BF16 = 0, 1
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_bytes", "fa_status_str",
+           "fa_version")
+STAGE_PREPROCESS, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 
 
 class Stride3(ctypes.Structure):
@@ -57,6 +59,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                            ctypes.POINTER(BwdStrides), vp, ctypes.c_size_t, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                  ctypes.POINTER(BwdStrides), vp, ctypes.c_size_t,
+                                  ctypes.c_uint, vp]
+    lib.fa_bwd_stages.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_str.argtypes = [i]

@@ -106,8 +106,14 @@ def workspace_bytes(B: int, H: int, N: int, D: int) -> int:
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
-        dq=None, dk=None, dv=None, workspace=None):
-    """Backward pass.  Returns (dq, dk, dv), each [B,N,H,D] in the input type."""
+        dq=None, dk=None, dv=None, workspace=None, stage_hook=None):
+    """Backward pass.  Returns (dq, dk, dv), each [B,N,H,D] in the input type.
+
+    ``stage_hook``: optional callable; when given, the three backward kernels
+    are enqueued one by one (fa_bwd_stages) and ``stage_hook(name)`` is called
+    before and after the dK/dV stage with name "dkdv_begin" / "dkdv_end"
+    (used to record stream events around that kernel).
+    """
     lib = _lib.load()
     B, N, H, D = _check_inputs(q, k, v, o, dout)
     q, k, v, o, dout = (_usable(t) for t in (q, k, v, o, dout))
@@ -124,13 +130,23 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib.BwdStrides(*(_stride3(t) for t in (q, k, v, o, dout, dq, dk, dv)))
-    status = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                        dv.data_ptr(), B, H, N, D, int(bool(causal)),
-                        _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
-                        workspace.data_ptr(), workspace.numel(), _stream(q))
-    if status != _lib.FA_OK:
-        _raise(status, "fa_bwd")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D,
+            int(bool(causal)), _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
+            workspace.data_ptr(), workspace.numel())
+    if stage_hook is None:
+        status = lib.fa_bwd(*args, _stream(q))
+        if status != _lib.FA_OK:
+            _raise(status, "fa_bwd")
+        return dq, dk, dv
+    for stage in (_lib.STAGE_PREPROCESS, _lib.STAGE_DKDV, _lib.STAGE_DQ):
+        if stage == _lib.STAGE_DKDV:
+            stage_hook("dkdv_begin")
+        status = lib.fa_bwd_stages(*args, stage, _stream(q))
+        if status != _lib.FA_OK:
+            _raise(status, "fa_bwd_stages")
+        if stage == _lib.STAGE_DKDV:
+            stage_hook("dkdv_end")
     return dq, dk, dv
 
 

@@ -93,10 +93,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int D) {
   return align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int D,
-           int causal, float scale, int dtype, const fa_bwd_strides* strides, void* workspace,
-           size_t workspace_bytes, hipStream_t stream) {
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                  int H, int N, int D, int causal, float scale, int dtype,
+                  const fa_bwd_strides* strides, void* workspace, size_t workspace_bytes,
+                  unsigned stages, hipStream_t stream) {
+  if (stages == 0 || (stages & ~FA_STAGE_ALL) != 0) return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID_ARG;
   int st = check_sizes(B, H, N, D, causal, scale, dtype);
@@ -143,8 +145,16 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   p.N = N;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
-  const hipError_t e = fa::launch_bwd(p, dtype, D, causal, stream);
+  const hipError_t e = fa::launch_bwd(p, dtype, D, causal, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int D,
+           int causal, float scale, int dtype, const fa_bwd_strides* strides, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_stages(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, causal, scale, dtype,
+                       strides, workspace, workspace_bytes, FA_STAGE_ALL, stream);
 }
 
 const char* fa_status_str(int status) {

@@ -272,31 +272,44 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 }
 
 template <typename T, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdParams& p_in, hipStream_t s) {
+static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream_t s) {
   BwdParams p = p_in;
   p.num_kblocks = (p.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
   const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
   constexpr int RPB = 256 / (D / 8);
   const unsigned row_blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3(row_blocks), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(256), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, s, p);
-  return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (stages & 1u) {
+    hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3(row_blocks), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (stages & 2u) {
+    const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (stages & 4u) {
+    hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, s, p);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
-hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
+                      hipStream_t s) {
   if (dtype == 1) {
-    if (D == 64) return causal ? launch_bwd_t<BF16, 64, true>(p, s) : launch_bwd_t<BF16, 64, false>(p, s);
-    return causal ? launch_bwd_t<BF16, 128, true>(p, s) : launch_bwd_t<BF16, 128, false>(p, s);
+    if (D == 64)
+      return causal ? launch_bwd_t<BF16, 64, true>(p, stages, s)
+                    : launch_bwd_t<BF16, 64, false>(p, stages, s);
+    return causal ? launch_bwd_t<BF16, 128, true>(p, stages, s)
+                  : launch_bwd_t<BF16, 128, false>(p, stages, s);
   }
-  if (D == 64) return causal ? launch_bwd_t<F16, 64, true>(p, s) : launch_bwd_t<F16, 64, false>(p, s);
-  return causal ? launch_bwd_t<F16, 128, true>(p, s) : launch_bwd_t<F16, 128, false>(p, s);
+  if (D == 64)
+    return causal ? launch_bwd_t<F16, 64, true>(p, stages, s)
+                  : launch_bwd_t<F16, 64, false>(p, stages, s);
+  return causal ? launch_bwd_t<F16, 128, true>(p, stages, s)
+                : launch_bwd_t<F16, 128, false>(p, stages, s);
 }
 
 }  // namespace fa

@@ -70,6 +70,18 @@ __device__ __forceinline__ u32x4 pack8(const float* v) {
                  pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7])};
 }
 
+// acc + lo(w) + hi(w) for a packed pair of halves w (v_dot2c_f32_{bf16,f16}).
+template <typename T>
+__device__ __forceinline__ float sum2_acc(uint32_t w, float acc) {
+  if constexpr (T::is_bf16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                  (f16x2){(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   if constexpr (T::is_bf16) {

@@ -80,8 +80,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
-  float m = -INFINITY;  // running max of scale*log2(e)*s over this row
-  float l = 0.0f;       // running sum of exp2(t - m), this lane's keys only
+  float m = -INFINITY;  // reference point (exp2 units) of this row's weights
+  float l = 0.0f;       // sum of the fp32 weights exp2(t - m), this lane's keys
+  float lb = 0.0f;      // sum of the same weights as rounded for the PV product
 
   const int qlast = min(qblk * BR + BR, N) - 1;
   const int ntiles = CAUSAL ? (qlast / BC + 1) : ((N + BC - 1) / BC);
@@ -142,29 +143,42 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
     }
     mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(m, mx * p.c);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    // The reference point m only moves when the tile max exceeds it by more
+    // than 2^8 (in exp2 units); otherwise p <= 256 and nothing is rescaled.
+    // O = sum p v / sum p and LSE = m + log2(sum p) hold for any m, so this
+    // changes no result, only how often the accumulator is rescaled.
+    const float mt = mx * p.c;
+    if (__any(mt > m + 8.0f)) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+      lb *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m = mnew;
+    }
 
-    float rs = 0.0f;
     u32x4 pb[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], p.c, -mnew));
-        rs += pv[i];
+        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], p.c, -m));
+        l += pv[i];
       }
       pb[nb][0] = pack8<T>(pv);
       pb[nb][1] = pack8<T>(pv + 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lb = sum2_acc<T>(pb[nb][0][w], lb);
+        lb = sum2_acc<T>(pb[nb][1][w], lb);
+      }
     }
-    l = l * alpha + rs;
-    m = mnew;
 
     // O^T += V^T P^T: A = V^T rows (d) from LDS, B = this lane's P values.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      oacc[db] *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -177,8 +191,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   }
 
   // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
+  // O is normalised by the sum of the weights exactly as the PV product used
+  // them (rounded to the input type), so each output row is a convex
+  // combination of V rows; the LSE uses the unrounded fp32 sum.
   const float lt = l + xor32(l);
-  const float inv = __builtin_amdgcn_rcpf(lt);
+  const float inv = __builtin_amdgcn_rcpf(lb + xor32(lb));
   if (qrow < N) {
     uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
 #pragma unroll

@@ -44,6 +44,8 @@ struct BwdParams {
 
 // dtype: 0 = f16, 1 = bf16.  Return the launch status.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s);
-hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, hipStream_t s);
+// stages: bit 0 preprocess, bit 1 dK/dV (+ dQ accumulation), bit 2 dQ conversion.
+hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
+                      hipStream_t s);
 
 }  // namespace fa

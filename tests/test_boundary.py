@@ -127,6 +127,13 @@ def test_bwd_rejects_before_launch():
     assert _bwd(strides=s) == _lib.FA_ERR_UNSUPPORTED
 
 
+def test_bwd_stages_rejects_bad_mask():
+    lib = _lib.load()
+    for stages in (0, 8, 15, 0xFFFFFFFF):
+        assert lib.fa_bwd_stages(*([P] * 9), 1, 1, 128, 64, 0, 0.125, _lib.FA_BF16, None, P,
+                                 1 << 40, stages, None) == _lib.FA_ERR_INVALID_ARG
+
+
 def test_python_binding_rejects_bad_inputs_without_gpu():
     q = torch.zeros(1, 16, 2, 64, dtype=torch.float32)
     with pytest.raises(fa.FaArgError, match="float16 / bfloat16"):
