@@ -11,7 +11,7 @@
 //
 // Three kernels:
 //   1. preprocess: Dvec = rowsum(dO o O) and zero the fp32 dQ accumulator;
-//   2. dK/dV: one workgroup per block of 128 keys (parallel over key blocks,
+//   2. dK/dV: one workgroup per block of keys (parallel over key blocks,
 //      batch and heads), K/V of its keys resident in registers, looping over
 //      query tiles; dQ contributions go to the fp32 accumulator with atomics;
 //   3. dQ conversion: scale, round to the input type, strided store.
@@ -48,34 +48,51 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------ kernel 2
-template <int D>
+//
+// Workgroup = NW wave64s; wave w owns the 32 keys kb0 + 32w .. +31 of the
+// workgroup's key block (BKV = 32*NW keys) and keeps their K and V rows in
+// registers as MFMA B operands, and their dK, dV accumulators.  The
+// workgroup walks the query tiles (64 rows each; causal: only tiles at or
+// after its first key).  Per tile, each wave computes
+//   S  = Q K^T, dP = dO V^T           (A: Q / dO rows from LDS)
+//   P  = exp2(S*c - LSE*log2 e),  dS = P o (dP - Dvec)
+//   dV += P^T dO, dK += dS^T Q        (B: dO / Q gathered transposed)
+// writes dS^T to LDS, and after the tile barrier the waves compute
+//   dQ(tile) = dS K                   (A: dS, B: K, both gathered transposed)
+// one 32x32 output block per wave over all BKV keys, so each dQ element
+// receives one fp32 atomic per workgroup.  The atomics of a tile are issued
+// in the next iteration, after that iteration's prefetch loads, so that no
+// load ever waits behind them.  Q, dO, LSE and Dvec of the next tile are
+// prefetched into registers during the current one (LDS double buffer, one
+// barrier per tile).
+template <int D, int NW>
 struct BwdCfg {
-  static constexpr int NW = 4;          // waves per workgroup
-  static constexpr int BKV = 32 * NW;   // keys per workgroup (32 per wave)
-  static constexpr int BQ = 32;         // query rows per iteration
-  static constexpr int KTP = BKV + 8;   // K^T row pitch
-  static constexpr int QP = D + 8;      // Q / dO row pitch
-  static constexpr int QTP = BQ + 8;    // Q^T / dO^T row pitch
-  static constexpr int SP = BKV + 8;    // dS row pitch
+  static constexpr int BKV = 32 * NW;   // keys per workgroup
+  static constexpr int BQ = 64;         // query rows per tile
+  static constexpr int NQB = BQ / 32;   // 32-row query blocks per tile
+  static constexpr int DB = D / 32;     // 32-wide d blocks
+  static constexpr int NBLK = NQB * DB; // 32x32 dQ blocks per tile
+  static constexpr int BPW = (NBLK + NW - 1) / NW;  // dQ blocks per wave
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int CPR = D / 8;     // 16-byte chunks per row
+  static constexpr int QPT = BQ * CPR / THREADS;    // Q (and dO) chunks per thread
+  static_assert(QPT * THREADS == BQ * CPR, "tile load must divide evenly");
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
-  using Cfg = BwdCfg<D>;
-  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ;
-  constexpr int KTP = Cfg::KTP, QP = Cfg::QP, QTP = Cfg::QTP, SP = Cfg::SP;
+template <typename T, int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
+  using Cfg = BwdCfg<D, NW>;
+  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NQB = Cfg::NQB, DB = Cfg::DB;
+  constexpr int NBLK = Cfg::NBLK, BPW = Cfg::BPW, THREADS = Cfg::THREADS;
+  constexpr int CPR = Cfg::CPR, QPT = Cfg::QPT;
   constexpr int KC = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int CPR = D / 8;
 
-  __shared__ __attribute__((aligned(16))) uint16_t KsT[D * KTP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t QsT[D * QTP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOsT[D * QTP];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[BQ * SP];
-  __shared__ float lse_s[BQ];
-  __shared__ float dvec_s[BQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[2][BKV * BQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dvec_s[2][BQ];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -114,18 +131,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     kreg[kc] = kv;
     vreg[kc] = vv;
   }
-  // K^T of the workgroup's keys (B operand of dQ = dS K).
-  for (int c = tid; c < BKV * CPR; c += 256) {
+  // The workgroup's K rows in LDS (B operand of dQ = dS K).
+  for (int c = tid; c < BKV * CPR; c += THREADS) {
     const int row = c / CPR;
     const int col = (c % CPR) * 8;
     const int kk = kb0 + row;
     u32x4 kv = {0u, 0u, 0u, 0u};
     if (kk < N) kv = ldg16(kbase + static_cast<int64_t>(kk) * p.sk.n + col);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      KsT[(col + 2 * w) * KTP + row] = static_cast<uint16_t>(kv[w] & 0xffffu);
-      KsT[(col + 2 * w + 1) * KTP + row] = static_cast<uint16_t>(kv[w] >> 16);
-    }
+    lds_write16(&Ks[tile_off<D>(row, col)], kv);
   }
 
   f32x16 dkacc[DB], dvacc[DB];
@@ -135,16 +148,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     dvacc[db] = (f32x16){};
   }
 
-  // Waves split the dQ = dS K product by d block (and by key half at D=64).
-  constexpr int WPD = Cfg::NW / DB;        // waves per d block
-  constexpr int KSL = BKV / 16 / WPD;      // 16-key slices per wave
-  const int dq_db = wave % DB;
-  const int dq_k0 = (wave / DB) * KSL * 16;
-
-  const int q_begin = CAUSAL ? kb0 : 0;
-  for (int qt = q_begin; qt < N; qt += BQ) {
-    __syncthreads();  // previous iteration fully consumed
-    for (int c = tid; c < BQ * CPR; c += 256) {
+  // Next-tile staging registers.
+  u32x4 pf_q[QPT], pf_do[QPT];
+  float pf_lse = INFINITY, pf_dvec = 0.0f;
+  auto load_tile = [&](int qt) {
+#pragma unroll
+    for (int it = 0; it < QPT; ++it) {
+      const int c = tid + THREADS * it;
       const int row = c / CPR;
       const int col = (c % CPR) * 8;
       const int q = qt + row;
@@ -153,85 +163,151 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         qv = ldg16(qbase + static_cast<int64_t>(q) * p.sq.n + col);
         dv = ldg16(dobase + static_cast<int64_t>(q) * p.sdo.n + col);
       }
-      lds_write16(&Qs[sigma32(row) * QP + col], qv);
-      lds_write16(&dOs[sigma32(row) * QP + col], dv);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        QsT[(col + 2 * w) * QTP + row] = static_cast<uint16_t>(qv[w] & 0xffffu);
-        QsT[(col + 2 * w + 1) * QTP + row] = static_cast<uint16_t>(qv[w] >> 16);
-        dOsT[(col + 2 * w) * QTP + row] = static_cast<uint16_t>(dv[w] & 0xffffu);
-        dOsT[(col + 2 * w + 1) * QTP + row] = static_cast<uint16_t>(dv[w] >> 16);
-      }
+      pf_q[it] = qv;
+      pf_do[it] = dv;
     }
     if (tid < BQ) {
       const int q = qt + tid;
-      lse_s[tid] = q < N ? lse_row[q] * kLog2e : INFINITY;  // padded rows: P = 0
-      dvec_s[tid] = q < N ? dvec_row[q] : 0.0f;
+      pf_lse = q < N ? lse_row[q] * kLog2e : INFINITY;  // padded rows: P = 0
+      pf_dvec = q < N ? dvec_row[q] : 0.0f;
     }
-    __syncthreads();
+  };
+  // Q / dO rows are stored under sigma_row so that the S and dP C layouts
+  // give each lane 8 consecutive query rows per 16-row slice.
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < QPT; ++it) {
+      const int c = tid + THREADS * it;
+      const int row = sigma_row(c / CPR);
+      const int col = (c % CPR) * 8;
+      lds_write16(&Qs[buf][tile_off<D>(row, col)], pf_q[it]);
+      lds_write16(&dOs[buf][tile_off<D>(row, col)], pf_do[it]);
+    }
+    if (tid < BQ) {
+      lse_s[buf][tid] = pf_lse;
+      dvec_s[buf][tid] = pf_dvec;
+    }
+  };
 
-    // S and dP for (query tile, this wave's 32 keys).  C value i of lane
-    // (l32, hh): query qt + c_item(i, hh), key = kw0 + l32.
-    f32x16 s = (f32x16){}, dp = (f32x16){};
+  f32x16 dqacc[BPW];
+  auto dq_atomics = [&](int qt) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      s = mfma32x32x16<T>(lds_read16(&Qs[l32 * QP + 16 * kc + 8 * hh]), kreg[kc], s);
-      dp = mfma32x32x16<T>(lds_read16(&dOs[l32 * QP + 16 * kc + 8 * hh]), vreg[kc], dp);
-    }
-    float pv[16], dsv[16];
+    for (int bi = 0; bi < BPW; ++bi) {
+      const int blk = wave + NW * bi;
+      if (blk < NBLK) {
+        const int qb = blk / DB, db = blk % DB;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qi = c_item(i, hh);
-      const int q = qt + qi;
-      float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -lse_s[qi]));
-      const bool valid = key < N && (!CAUSAL || key <= q);
-      pr = valid ? pr : 0.0f;
-      pv[i] = pr;
-      dsv[i] = pr * (dp[i] - dvec_s[qi]);
-    }
-    const u32x4 pP[2] = {pack8<T>(pv), pack8<T>(pv + 8)};
-    const u32x4 pS[2] = {pack8<T>(dsv), pack8<T>(dsv + 8)};
-
-    // dV += P^T dO and dK += dS^T Q: A = this lane's P / dS values (rows =
-    // keys), B = dO^T / Q^T rows (d) from LDS.
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int off = (32 * db + l32) * QTP + 16 * cc + 8 * hh;
-        dvacc[db] = mfma32x32x16<T>(pP[cc], lds_read16(&dOsT[off]), dvacc[db]);
-        dkacc[db] = mfma32x32x16<T>(pS[cc], lds_read16(&QsT[off]), dkacc[db]);
+        for (int i = 0; i < 16; ++i) {
+          const int q = qt + 32 * qb + c_row(i, hh);
+          if (q < N) atomicAdd(dq_acc + static_cast<int64_t>(q) * D + 32 * db + l32, dqacc[bi][i]);
+        }
       }
     }
+  };
 
-    // dS (rounded like the MFMA operands) to LDS as [query][key].
+  const int q_begin = CAUSAL ? kb0 : 0;
+  const int ntiles = (N - q_begin + BQ - 1) / BQ;
+  load_tile(q_begin);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const int qt = q_begin + t * BQ;
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) load_tile(qt + BQ);
+    if (t > 0) dq_atomics(qt - BQ);
+
+    // ---- S, dP, P, dS, dV, dK for this wave's 32 keys
+    u32x4 pS[NQB][2];
+    const bool active = !CAUSAL || (qt + BQ - 1 >= kw0);
+    if (active) {
+      const bool need_mask = (CAUSAL && kw0 + 31 > qt) || (kw0 + 31 >= N);
+      u32x4 pP[NQB][2];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
+      for (int qb = 0; qb < NQB; ++qb) {
+        f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t pair = pS[cc][w];
-        const int i0 = 8 * cc + 2 * w;
-        dSs[c_item(i0, hh) * SP + 32 * wave + l32] = static_cast<uint16_t>(pair & 0xffffu);
-        dSs[c_item(i0 + 1, hh) * SP + 32 * wave + l32] = static_cast<uint16_t>(pair >> 16);
+        for (int kc = 0; kc < KC; ++kc) {
+          const int off = tile_off<D>(32 * qb + l32, 16 * kc + 8 * hh);
+          s = mfma32x32x16<T>(lds_read16(&Qs[cur][off]), kreg[kc], s);
+          dp = mfma32x32x16<T>(lds_read16(&dOs[cur][off]), vreg[kc], dp);
+        }
+        // C value i: query qt + 32*qb + c_item(i, hh), key = this lane's key.
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int r0 = 32 * qb + 16 * c + 8 * hh;
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[cur][r0]);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[cur][r0 + 4]);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dvec_s[cur][r0]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dvec_s[cur][r0 + 4]);
+          float pv[8], dsv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = 8 * c + e;
+            const float lse2 = e < 4 ? l0[e] : l1[e - 4];
+            const float dvq = e < 4 ? d0[e] : d1[e - 4];
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -lse2));
+            if (need_mask) {
+              const int q = qt + r0 + e;
+              const bool valid = key < N && (!CAUSAL || key <= q);
+              pr = valid ? pr : 0.0f;
+            }
+            pv[e] = pr;
+            dsv[e] = pr * (dp[i] - dvq);
+          }
+          pP[qb][c] = pack8<T>(pv);
+          pS[qb][c] = pack8<T>(dsv);
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q over the tile's 64 query rows.
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x4 bdo = tr_operand<D, true>(dOs[cur], 32 * qb + 16 * c, 32 * db, lane);
+            dvacc[db] = mfma32x32x16<T>(pP[qb][c], bdo, dvacc[db]);
+            const u32x4 bq = tr_operand<D, true>(Qs[cur], 32 * qb + 16 * c, 32 * db, lane);
+            dkacc[db] = mfma32x32x16<T>(pS[qb][c], bq, dkacc[db]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) pS[qb][0] = pS[qb][1] = (u32x4){0u, 0u, 0u, 0u};
+    }
+
+    // ---- dS^T (as rounded for the MFMAs) to LDS: row = key, 64 query columns.
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        lds_write16(&dSt[cur][tile_off<BQ>(32 * wave + l32, 32 * qb + 16 * c + 8 * hh)], pS[qb][c]);
       }
     }
+    if (has_next) store_tile(cur ^ 1);
     __syncthreads();
 
-    // dQ partial for this query tile over the workgroup's keys.
-    f32x16 dqacc = (f32x16){};
+    // ---- dQ(tile) = dS K over the workgroup's keys, one 32x32 block per wave.
 #pragma unroll
-    for (int ks = 0; ks < KSL; ++ks) {
-      const int kk = dq_k0 + 16 * ks;
-      const u32x4 a = lds_read16(&dSs[l32 * SP + kk + 8 * hh]);
-      const u32x4 bb = lds_read16(&KsT[(32 * dq_db + l32) * KTP + kk + 8 * hh]);
-      dqacc = mfma32x32x16<T>(a, bb, dqacc);
-    }
+    for (int bi = 0; bi < BPW; ++bi) {
+      const int blk = wave + NW * bi;
+      f32x16 acc = (f32x16){};
+      if (blk < NBLK) {
+        const int qb = blk / DB, db = blk % DB;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = qt + c_row(i, hh);
-      if (q < N) atomicAdd(dq_acc + static_cast<int64_t>(q) * D + 32 * dq_db + l32, dqacc[i]);
+        for (int ks = 0; ks < BKV / 16; ++ks) {
+          const u32x4 a = tr_operand<BQ, false>(dSt[cur], 16 * ks, 32 * qb, lane);
+          const u32x4 bk = tr_operand<D, false>(Ks, 16 * ks, 32 * db, lane);
+          acc = mfma32x32x16<T>(a, bk, acc);
+        }
+      }
+      dqacc[bi] = acc;
     }
   }
+  dq_atomics(q_begin + (ntiles - 1) * BQ);
 
   // Epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO.  C value i: key
   // kw0 + c_row(i, hh), d = 32*db + l32.
@@ -250,6 +326,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 }
+
+// Waves per workgroup of the dK/dV kernel: 8 at head_dim 64 (256 keys per
+// workgroup halves the dQ atomics), 4 at head_dim 128 (register budget).
+template <int D>
+struct BwdWaves {
+  static constexpr int NW = D == 64 ? 8 : 4;
+};
 
 // ------------------------------------------------------------------ kernel 3
 template <typename T, int D>
@@ -273,8 +356,9 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream_t s) {
+  constexpr int NW = BwdWaves<D>::NW;
   BwdParams p = p_in;
-  p.num_kblocks = (p.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
+  p.num_kblocks = (p.N + BwdCfg<D, NW>::BKV - 1) / BwdCfg<D, NW>::BKV;
   const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
   constexpr int RPB = 256 / (D / 8);
   const unsigned row_blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
@@ -285,8 +369,8 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   }
   if (stages & 2u) {
     const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * NW), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4u) {

@@ -117,11 +117,6 @@ __device__ __forceinline__ void lds_write16(uint16_t* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
-// Value of lane (L ^ 32): exchange between the two 32-lane halves.
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
-}
-
 // Permutation of the 32 rows of an MFMA A operand that makes the C layout of
 // the product give each lane 8 consecutive row indices per 16-row slice:
 // swaps bits 2 and 3 of the row index (an involution).  With A row m holding
@@ -135,6 +130,75 @@ __host__ __device__ constexpr int c_item(int i, int hh) {
 // Row of C value i of lane half hh when A rows are in natural order.
 __host__ __device__ constexpr int c_row(int i, int hh) {
   return 8 * (i / 4) + 4 * hh + (i % 4);
+}
+
+// sigma32 applied to the low 5 bits of a tile row index.
+__device__ __forceinline__ int sigma_row(int r) { return (r & ~31) | sigma32(r & 31); }
+
+// ---------------------------------------------------------------- LDS tiles
+//
+// Tiles are stored row-major with W halves per row (W = 64 or 128, no
+// padding) and the 16-byte chunks of each row XOR-swizzled by a function of
+// the row.  The swizzle keeps two access patterns free of bank conflicts on
+// the 64-bank LDS:
+//   * row reads (ds_read_b128): 16 consecutive rows, same logical chunk;
+//   * transposed reads (ds_read_b64_tr_b16): 4 consecutive rows starting at
+//     a multiple of 4, an aligned block of 4 logical chunks.
+// W = 64 (8 chunks, two rows per 256-byte bank line): g(r) = bitrev3(r/2 % 8).
+// W = 128 (16 chunks, one row per bank line): g(r) = bitrev4(r % 16).
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(W == 64 || W == 128, "tile width");
+  if constexpr (W == 64) {
+    const int u = (r >> 1) & 7;
+    return ((u & 1) << 2) | (u & 2) | ((u >> 2) & 1);
+  } else {
+    const int u = r & 15;
+    return ((u & 1) << 3) | ((u & 2) << 1) | ((u & 4) >> 1) | ((u & 8) >> 3);
+  }
+}
+// Element offset of (row r, column col) in a swizzled tile of width W.
+template <int W>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * W + ((((col >> 3) ^ swz<W>(r)) << 3) | (col & 7));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4 __attribute__((address_space(3))) * lds_s16x4_ptr;
+
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA 32x32x16 operand gathered "transposed" from a k-major swizzled tile
+// X[k][n] (row = k, n contiguous): lane L receives X[k0 + 8*(L/32) + e]
+// [n0 + L%32], e = 0..7 -- the B operand for X = B[k][n], or the A operand
+// A[m][k] = X[k][m].
+//
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group receives
+// as its element j the (i%4)-th half of the 8 bytes addressed by lane
+// 4j + i/4 of the same group.  So lane s of group G addresses row
+// k0 + 8*(G/2) + s/4 (+4 for the second read) at column n0 + 16*(G%2) + 4*(s%4).
+// With SIGMA_ROWS the tile stores logical row r at row sigma_row(r).
+template <int W, bool SIGMA_ROWS>
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int k0, int n0, int lane) {
+  const int G = lane >> 4, s = lane & 15;
+  int r0 = k0 + 8 * (G >> 1) + (s >> 2);
+  int r1 = r0 + 4;
+  if constexpr (SIGMA_ROWS) {
+    r0 = sigma_row(r0);
+    r1 = sigma_row(r1);
+  }
+  const int col = n0 + 16 * (G & 1) + 4 * (s & 3);
+  const u32x2 lo = lds_read_tr8(tile + tile_off<W>(r0, col));
+  const u32x2 hi = lds_read_tr8(tile + tile_off<W>(r1, col));
+  return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Value of lane (L ^ 32): exchange between the two 32-lane halves.
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
 }
 
 }  // namespace fa

@@ -12,40 +12,45 @@
 // Parallelism runs over (batch, head, query block) as in section 3.2 of the
 // same walkthrough; causal tiles above the diagonal are skipped.
 //
-// Work split: a workgroup of 4 wave64s owns 128 query rows, 32 per wave.
+// Work split: a workgroup of NW wave64s owns 32*NW query rows, 32 per wave.
 // Each wave computes S^T = K Q^T for its rows (K from LDS as the A operand,
 // its Q rows held in registers as the B operand), so the C layout of S^T
 // leaves one query row per lane -- the row max, the rescale factor and the
 // output rescale are then per-lane scalars.  K rows are stored in LDS under
 // the sigma32 row permutation so that the P values a lane holds are exactly
-// the B operand of the next product O^T += V^T P^T, with no data movement.
+// the B operand of the next product O^T += V^T P^T, with no data movement;
+// that product's A operand V^T is gathered from the natural-layout V tile by
+// transposing LDS reads.  K/V tiles of 64 keys are double-buffered: the next
+// tile is loaded into registers while the current one is consumed, so there
+// is one barrier per tile.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 
-template <int D>
+template <int D, int NW>
 struct FwdCfg {
-  static constexpr int NW = 4;        // waves per workgroup
   static constexpr int BR = 32 * NW;  // query rows per workgroup
   static constexpr int BC = 64;       // keys per K/V tile
-  static constexpr int KP = D + 8;    // K tile row pitch (elements)
-  static constexpr int VP = BC + 8;   // V^T tile row pitch (elements)
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
+  static constexpr int NCH = BC * CPR / THREADS;  // chunks per thread per tensor
+  static_assert(NCH * THREADS == BC * CPR, "tile load must divide evenly");
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
-  using Cfg = FwdCfg<D>;
-  constexpr int BR = Cfg::BR, BC = Cfg::BC, KP = Cfg::KP, VP = Cfg::VP;
+template <typename T, int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
+  using Cfg = FwdCfg<D, NW>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, THREADS = Cfg::THREADS;
+  constexpr int CPR = Cfg::CPR, NCH = Cfg::NCH;
   constexpr int KC = D / 16;   // 16-wide k slices of Q K^T
   constexpr int NB = BC / 32;  // 32-key blocks per tile
   constexpr int DB = D / 32;   // 32-wide d blocks of O
-  constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
-  constexpr int NCH = BC * CPR / 256;
-  static_assert(NCH * 256 == BC * CPR, "tile load must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  // Double-buffered K and V tiles, natural [key][d] layout, swizzled chunks;
+  // K rows additionally stored under sigma_row.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -55,7 +60,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 
   const int BH = p.B * p.H;
   const int bh = blockIdx.x % BH;
-  const int qblk = p.num_qblocks - 1 - static_cast<int>(blockIdx.x / BH);
+  const int qblk = p.num_qblocks - 1 - static_cast<int>(blockIdx.x / BH);  // heaviest first
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;
@@ -87,107 +92,127 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   const int qlast = min(qblk * BR + BR, N) - 1;
   const int ntiles = CAUSAL ? (qlast / BC + 1) : ((N + BC - 1) / BC);
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = j * BC;
-    __syncthreads();  // previous tile fully consumed
+  u32x4 pf_k[NCH], pf_v[NCH];
+  auto load_tile = [&](int kv0) {
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      const int c = tid + 256 * it;
-      const int row = c / CPR;
+      const int c = tid + THREADS * it;
+      const int key = kv0 + c / CPR;
       const int col = (c % CPR) * 8;
-      const int key = kv0 + row;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (key < N) {
         kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + col);
         vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + col);
       }
-      const int lrow = (row & ~31) | sigma32(row & 31);
-      lds_write16(&Ks[lrow * KP + col], kv);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        Vt[(col + 2 * w) * VP + row] = static_cast<uint16_t>(vv[w] & 0xffffu);
-        Vt[(col + 2 * w + 1) * VP + row] = static_cast<uint16_t>(vv[w] >> 16);
-      }
+      pf_k[it] = kv;
+      pf_v[it] = vv;
     }
-    __syncthreads();
-
-    // S^T blocks: C value i of lane (l32, hh) is the score of query qrow
-    // against key kv0 + 32*nb + c_item(i, hh).
-    f32x16 sacc[NB];
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      sacc[nb] = (f32x16){};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 a = lds_read16(&Ks[(32 * nb + l32) * KP + 16 * kc + 8 * hh]);
-        sacc[nb] = mfma32x32x16<T>(a, qreg[kc], sacc[nb]);
-      }
+    for (int it = 0; it < NCH; ++it) {
+      const int c = tid + THREADS * it;
+      const int row = c / CPR;
+      const int col = (c % CPR) * 8;
+      lds_write16(&Ks[buf][tile_off<D>(sigma_row(row), col)], pf_k[it]);
+      lds_write16(&Vs[buf][tile_off<D>(row, col)], pf_v[it]);
     }
+  };
 
-    const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
-    if (need_mask) {
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
+    const int kv0 = j * BC;
+    const bool has_next = j + 1 < ntiles;
+    if (has_next) load_tile(kv0 + BC);
+
+    // Causal: tiles entirely above this wave's rows carry no weight for it.
+    if (!CAUSAL || kv0 <= q0 + 31) {
+      // S^T blocks: C value i of lane (l32, hh) is the score of query qrow
+      // against key kv0 + 32*nb + c_item(i, hh).
+      f32x16 sacc[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
+        sacc[nb] = (f32x16){};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const u32x4 a = lds_read16(&Ks[cur][tile_off<D>(32 * nb + l32, 16 * kc + 8 * hh)]);
+          sacc[nb] = mfma32x32x16<T>(a, qreg[kc], sacc[nb]);
+        }
+      }
+
+      const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + 32 * nb + c_item(i, hh);
+            if (key >= N || (CAUSAL && key > qrow)) sacc[nb][i] = -INFINITY;
+          }
+        }
+      }
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
+      }
+      mx = fmaxf(mx, xor32(mx));
+      // The reference point m only moves when the tile max exceeds it by more
+      // than 2^8 (in exp2 units); otherwise p <= 256 and nothing is rescaled.
+      // O = sum p v / sum p and LSE = m + log2(sum p) hold for any m, so this
+      // changes no result, only how often the accumulator is rescaled.
+      const float mt = mx * p.c;
+      if (__any(mt > m + 8.0f)) {
+        const float mnew = fmaxf(m, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+        lb *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m = mnew;
+      }
+
+      u32x4 pb[NB][2];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * nb + c_item(i, hh);
-          if (key >= N || (CAUSAL && key > qrow)) sacc[nb][i] = -INFINITY;
+          pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], p.c, -m));
+          l += pv[i];
+        }
+        pb[nb][0] = pack8<T>(pv);
+        pb[nb][1] = pack8<T>(pv + 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          lb = sum2_acc<T>(pb[nb][0][w], lb);
+          lb = sum2_acc<T>(pb[nb][1][w], lb);
+        }
+      }
+
+      // O^T += V^T P^T: A = V^T gathered transposed from the V tile, B = this
+      // lane's P values (keys 32*nb + 16*cc + 8*hh + 0..7).
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const u32x4 a = tr_operand<D, false>(Vs[cur], 32 * nb + 16 * cc, 32 * db, lane);
+            oacc[db] = mfma32x32x16<T>(a, pb[nb][cc], oacc[db]);
+          }
         }
       }
     }
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
-    }
-    mx = fmaxf(mx, xor32(mx));
-    // The reference point m only moves when the tile max exceeds it by more
-    // than 2^8 (in exp2 units); otherwise p <= 256 and nothing is rescaled.
-    // O = sum p v / sum p and LSE = m + log2(sum p) hold for any m, so this
-    // changes no result, only how often the accumulator is rescaled.
-    const float mt = mx * p.c;
-    if (__any(mt > m + 8.0f)) {
-      const float mnew = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
-      lb *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m = mnew;
-    }
-
-    u32x4 pb[NB][2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], p.c, -m));
-        l += pv[i];
-      }
-      pb[nb][0] = pack8<T>(pv);
-      pb[nb][1] = pack8<T>(pv + 8);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        lb = sum2_acc<T>(pb[nb][0][w], lb);
-        lb = sum2_acc<T>(pb[nb][1][w], lb);
-      }
-    }
-
-    // O^T += V^T P^T: A = V^T rows (d) from LDS, B = this lane's P values.
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const u32x4 a = lds_read16(&Vt[(32 * db + l32) * VP + 32 * nb + 16 * cc + 8 * hh]);
-          oacc[db] = mfma32x32x16<T>(a, pb[nb][cc], oacc[db]);
-        }
-      }
-    }
+    if (has_next) store_tile(cur ^ 1);
+    __syncthreads();
   }
 
   // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
@@ -214,14 +239,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_fwd_t(const FwdParams& p_in, hipStream_t s) {
+template <typename T, int D, int NW, bool CAUSAL>
+static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   FwdParams p = p_in;
-  p.num_qblocks = (p.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
+  p.num_qblocks = (p.N + FwdCfg<D, NW>::BR - 1) / FwdCfg<D, NW>::BR;
   const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_qblocks;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * NW), 0, s, p);
   return hipGetLastError();
+}
+
+// 8 waves (256 query rows) per workgroup when that still gives at least two
+// workgroups per compute unit, else 4 waves (128 rows).
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
+  const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
+  if (wg8 >= 512) return launch_fwd_nw<T, D, 8, CAUSAL>(p, s);
+  return launch_fwd_nw<T, D, 4, CAUSAL>(p, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s) {
