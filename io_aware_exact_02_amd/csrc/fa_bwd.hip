@@ -86,13 +86,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NBLK = Cfg::NBLK, BPW = Cfg::BPW, THREADS = Cfg::THREADS;
   constexpr int CPR = Cfg::CPR, QPT = Cfg::QPT;
   constexpr int KC = D / 16;
+  constexpr int QTILE = BQ * D;    // halves per Q (or dO) buffer
+  constexpr int STILE = BKV * BQ;  // halves per dS^T buffer
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t dSt[2][BKV * BQ];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dvec_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2 * QTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2 * QTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[2 * STILE];
+  __shared__ __attribute__((aligned(16))) float lse_s[2 * BQ];  // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float ndv_s[2 * BQ];  // -Dvec
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -106,11 +108,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;
+  const float c_scale = p.c;
 
-  const uint16_t* qbase = p.q + b * p.sq.b + h * p.sq.h;
   const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
   const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
-  const uint16_t* dobase = p.dout + b * p.sdo.b + h * p.sdo.h;
   const float* lse_row = p.lse + static_cast<int64_t>(bh) * N;
   const float* dvec_row = p.dvec + static_cast<int64_t>(bh) * N;
   float* dq_acc = p.dq_accum + static_cast<int64_t>(bh) * N * D;
@@ -141,6 +142,84 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     lds_write16(&Ks[tile_off<D>(row, col)], kv);
   }
 
+  // ---- per-lane LDS offsets (bytes), fixed for the whole kernel
+  uint32_t q_off[KC];  // row reads of Q / dO (A of S, dP); + 32*qb rows
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) q_off[kc] = row_off<D>(lane, kc);
+  uint32_t qt_off[2][DB];  // transposed reads of Q / dO (B of dK, dV)
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) qt_off[t][db] = tr_off<D, true>(lane, t, db);
+  // dS^T rows written by this wave: row 32*wave + l32, query chunk 2*(2qb+c) + hh.
+  const uint32_t ds_w = static_cast<uint32_t>((32 * wave + l32) * 2 * BQ +
+                                              16 * (hh ^ swz<BQ>(l32)));
+  // This wave's dQ blocks: transposed reads of dS (A) and K (B).
+  uint32_t s_off[BPW][2], kt_off[BPW][2];
+#pragma unroll
+  for (int bi = 0; bi < BPW; ++bi) {
+    const int blk = (wave + NW * bi) % NBLK;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s_off[bi][t] = tr_off<BQ, false>(lane, t, blk / DB);
+      kt_off[bi][t] = tr_off<D, false>(lane, t, blk % DB);
+    }
+  }
+
+  // ---- next-tile staging: global pointers, LDS offsets, registers
+  const int q_begin = CAUSAL ? kb0 : 0;
+  const int ntiles = (N - q_begin + BQ - 1) / BQ;
+  const uint16_t* qptr[QPT];
+  const uint16_t* doptr[QPT];
+  int ld_row[QPT];
+  uint32_t st_off[QPT];
+#pragma unroll
+  for (int it = 0; it < QPT; ++it) {
+    const int c = tid + THREADS * it;
+    const int row = c / CPR;
+    const int col = (c % CPR) * 8;
+    ld_row[it] = q_begin + row;
+    qptr[it] = p.q + b * p.sq.b + h * p.sq.h + static_cast<int64_t>(q_begin + row) * p.sq.n + col;
+    doptr[it] = p.dout + b * p.sdo.b + h * p.sdo.h +
+                static_cast<int64_t>(q_begin + row) * p.sdo.n + col;
+    // Q / dO rows are stored under sigma_row so that the S and dP C layouts
+    // give each lane 8 consecutive query rows per 16-row slice.
+    st_off[it] = 2 * tile_off<D>(sigma_row(row), col);
+  }
+  const int64_t q_step = static_cast<int64_t>(BQ) * p.sq.n;
+  const int64_t do_step = static_cast<int64_t>(BQ) * p.sdo.n;
+  u32x4 pf_q[QPT], pf_do[QPT];
+  float pf_lse = INFINITY, pf_ndv = 0.0f;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int it = 0; it < QPT; ++it) {
+      u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
+      if (ld_row[it] + t * BQ < N) {
+        qv = ldg16(qptr[it] + t * q_step);
+        dv = ldg16(doptr[it] + t * do_step);
+      }
+      pf_q[it] = qv;
+      pf_do[it] = dv;
+    }
+    if (tid < BQ) {
+      const int q = q_begin + t * BQ + tid;
+      pf_lse = q < N ? lse_row[q] * kLog2e : INFINITY;  // padded rows: P = 0
+      pf_ndv = q < N ? -dvec_row[q] : 0.0f;
+    }
+  };
+  auto store_tile = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+#pragma unroll
+    for (int it = 0; it < QPT; ++it) {
+      lds_st16(Qs + BUF * QTILE, st_off[it], pf_q[it]);
+      lds_st16(dOs + BUF * QTILE, st_off[it], pf_do[it]);
+    }
+    if (tid < BQ) {
+      lse_s[BUF * BQ + tid] = pf_lse;
+      ndv_s[BUF * BQ + tid] = pf_ndv;
+    }
+  };
+
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -148,47 +227,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     dvacc[db] = (f32x16){};
   }
 
-  // Next-tile staging registers.
-  u32x4 pf_q[QPT], pf_do[QPT];
-  float pf_lse = INFINITY, pf_dvec = 0.0f;
-  auto load_tile = [&](int qt) {
-#pragma unroll
-    for (int it = 0; it < QPT; ++it) {
-      const int c = tid + THREADS * it;
-      const int row = c / CPR;
-      const int col = (c % CPR) * 8;
-      const int q = qt + row;
-      u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
-      if (q < N) {
-        qv = ldg16(qbase + static_cast<int64_t>(q) * p.sq.n + col);
-        dv = ldg16(dobase + static_cast<int64_t>(q) * p.sdo.n + col);
-      }
-      pf_q[it] = qv;
-      pf_do[it] = dv;
-    }
-    if (tid < BQ) {
-      const int q = qt + tid;
-      pf_lse = q < N ? lse_row[q] * kLog2e : INFINITY;  // padded rows: P = 0
-      pf_dvec = q < N ? dvec_row[q] : 0.0f;
-    }
-  };
-  // Q / dO rows are stored under sigma_row so that the S and dP C layouts
-  // give each lane 8 consecutive query rows per 16-row slice.
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < QPT; ++it) {
-      const int c = tid + THREADS * it;
-      const int row = sigma_row(c / CPR);
-      const int col = (c % CPR) * 8;
-      lds_write16(&Qs[buf][tile_off<D>(row, col)], pf_q[it]);
-      lds_write16(&dOs[buf][tile_off<D>(row, col)], pf_do[it]);
-    }
-    if (tid < BQ) {
-      lse_s[buf][tid] = pf_lse;
-      dvec_s[buf][tid] = pf_dvec;
-    }
-  };
-
+  // ---- dQ: one 32x32 block per wave per tile, added with fp32 atomics.
+  // C value i of block (qb, db): query qt + 32*qb + c_row(i, hh), d = 32*db + l32.
   f32x16 dqacc[BPW];
   auto dq_atomics = [&](int qt) {
 #pragma unroll
@@ -196,116 +236,139 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       const int blk = wave + NW * bi;
       if (blk < NBLK) {
         const int qb = blk / DB, db = blk % DB;
+        const int qr = qt + 32 * qb + 4 * hh;
+        float* base = dq_acc + static_cast<int64_t>(qr) * D + 32 * db + l32;
+        if (qt + 32 * qb + 31 < N) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = qt + 32 * qb + c_row(i, hh);
-          if (q < N) atomicAdd(dq_acc + static_cast<int64_t>(q) * D + 32 * db + l32, dqacc[bi][i]);
+          for (int i = 0; i < 16; ++i)
+            atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, dqacc[bi][i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (qr + 8 * (i / 4) + (i % 4) < N)
+              atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, dqacc[bi][i]);
         }
       }
     }
   };
 
-  const int q_begin = CAUSAL ? kb0 : 0;
-  const int ntiles = (N - q_begin + BQ - 1) / BQ;
-  load_tile(q_begin);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const int qt = q_begin + t * BQ;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(qt + BQ);
-    if (t > 0) dq_atomics(qt - BQ);
-
-    // ---- S, dP, P, dS, dV, dK for this wave's 32 keys
-    u32x4 pS[NQB][2];
-    const bool active = !CAUSAL || (qt + BQ - 1 >= kw0);
-    if (active) {
-      const bool need_mask = (CAUSAL && kw0 + 31 > qt) || (kw0 + 31 >= N);
-      u32x4 pP[NQB][2];
+  // ---- S, dP, P, dS, dV, dK for this wave's 32 keys and one query tile.
+  auto compute = [&](auto bufc, auto maskc, int qt, u32x4 (&pS)[NQB][2]) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASK = decltype(maskc)::value;
+    const uint16_t* qs = Qs + BUF * QTILE;
+    const uint16_t* dos = dOs + BUF * QTILE;
+    const float* ls = lse_s + BUF * BQ + 8 * hh;
+    const float* nd = ndv_s + BUF * BQ + 8 * hh;
+    u32x4 pP[NQB][2];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        f32x16 s = (f32x16){}, dp = (f32x16){};
+    for (int qb = 0; qb < NQB; ++qb) {
+      // C value i: query qt + 32*qb + c_item(i, hh), key = this lane's key.
+      // dP starts from -Dvec of its query so that the product yields dP - Dvec.
+      const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd + 32 * qb);
+      const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 32 * qb + 4);
+      const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 32 * qb + 16);
+      const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 32 * qb + 20);
+      f32x16 dp = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                   n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+      f32x16 s = (f32x16){};
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const int off = tile_off<D>(32 * qb + l32, 16 * kc + 8 * hh);
-          s = mfma32x32x16<T>(lds_read16(&Qs[cur][off]), kreg[kc], s);
-          dp = mfma32x32x16<T>(lds_read16(&dOs[cur][off]), vreg[kc], dp);
-        }
-        // C value i: query qt + 32*qb + c_item(i, hh), key = this lane's key.
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int r0 = 32 * qb + 16 * c + 8 * hh;
-          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[cur][r0]);
-          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[cur][r0 + 4]);
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dvec_s[cur][r0]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dvec_s[cur][r0 + 4]);
-          float pv[8], dsv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 8 * c + e;
-            const float lse2 = e < 4 ? l0[e] : l1[e - 4];
-            const float dvq = e < 4 ? d0[e] : d1[e - 4];
-            float pr = __builtin_amdgcn_exp2f(fmaf(s[i], p.c, -lse2));
-            if (need_mask) {
-              const int q = qt + r0 + e;
-              const bool valid = key < N && (!CAUSAL || key <= q);
-              pr = valid ? pr : 0.0f;
-            }
-            pv[e] = pr;
-            dsv[e] = pr * (dp[i] - dvq);
-          }
-          pP[qb][c] = pack8<T>(pv);
-          pS[qb][c] = pack8<T>(dsv);
-        }
+      for (int kc = 0; kc < KC; ++kc) {
+        s = mfma32x32x16<T>(lds_ld16(qs + 32 * qb * D, q_off[kc]), kreg[kc], s);
+        dp = mfma32x32x16<T>(lds_ld16(dos + 32 * qb * D, q_off[kc]), vreg[kc], dp);
       }
-      // dV += P^T dO, dK += dS^T Q over the tile's 64 query rows.
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * qb);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 4);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 16);
+      const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 20);
+      const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
+                            l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
+      float pv[16], dsv[16];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const u32x4 bdo = tr_operand<D, true>(dOs[cur], 32 * qb + 16 * c, 32 * db, lane);
-            dvacc[db] = mfma32x32x16<T>(pP[qb][c], bdo, dvacc[db]);
-            const u32x4 bq = tr_operand<D, true>(Qs[cur], 32 * qb + 16 * c, 32 * db, lane);
-            dkacc[db] = mfma32x32x16<T>(pS[qb][c], bq, dkacc[db]);
-          }
+      for (int i = 0; i < 16; ++i) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[i], c_scale, -lv[i]));
+        if constexpr (MASK) {
+          const int q = qt + 32 * qb + c_item(i, hh);
+          const bool valid = key < N && (!CAUSAL || key <= q);
+          pr = valid ? pr : 0.0f;
         }
+        pv[i] = pr;
+        dsv[i] = pr * dp[i];
       }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) pS[qb][0] = pS[qb][1] = (u32x4){0u, 0u, 0u, 0u};
+      pP[qb][0] = pack8<T>(pv);
+      pP[qb][1] = pack8<T>(pv + 8);
+      pS[qb][0] = pack8<T>(dsv);
+      pS[qb][1] = pack8<T>(dsv + 8);
     }
-
-    // ---- dS^T (as rounded for the MFMAs) to LDS: row = key, 64 query columns.
+    // dV += P^T dO, dK += dS^T Q over the tile's query rows.
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        lds_write16(&dSt[cur][tile_off<BQ>(32 * wave + l32, 32 * qb + 16 * c + 8 * hh)], pS[qb][c]);
+        const int r = 32 * qb + 16 * c;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 bdo = lds_tr16(dos + r * D, qt_off[0][db], qt_off[1][db]);
+          dvacc[db] = mfma32x32x16<T>(pP[qb][c], bdo, dvacc[db]);
+          const u32x4 bq = lds_tr16(qs + r * D, qt_off[0][db], qt_off[1][db]);
+          dkacc[db] = mfma32x32x16<T>(pS[qb][c], bq, dkacc[db]);
+        }
       }
     }
-    if (has_next) store_tile(cur ^ 1);
+  };
+
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int qt = q_begin + t * BQ;
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) load_tile(t + 1);
+    if (t > 0) dq_atomics(qt - BQ);
+
+    u32x4 pS[NQB][2];
+    if (!CAUSAL || qt + BQ - 1 >= kw0) {
+      const bool need_mask = (CAUSAL && kw0 + 31 > qt) || (kw0 + 31 >= N);
+      if (need_mask) {
+        compute(bufc, IntC<1>{}, qt, pS);
+      } else {
+        compute(bufc, IntC<0>{}, qt, pS);
+      }
+    } else {  // causal: every key of this wave lies after every query of the tile
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) pS[qb][0] = pS[qb][1] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    // dS^T (as rounded for the MFMAs) to LDS: row = key, query columns.
+    uint16_t* dst = dSt + BUF * STILE;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) lds_st16(dst, ds_w ^ (64 * qb + 32 * c), pS[qb][c]);
+    }
+    if (has_next) store_tile(IntC<BUF ^ 1>{});
     __syncthreads();
 
-    // ---- dQ(tile) = dS K over the workgroup's keys, one 32x32 block per wave.
+    // dQ(tile) = dS K over the workgroup's keys.
+    const uint16_t* sts = dSt + BUF * STILE;
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
-      const int blk = wave + NW * bi;
       f32x16 acc = (f32x16){};
-      if (blk < NBLK) {
-        const int qb = blk / DB, db = blk % DB;
+      if (wave + NW * bi < NBLK) {
 #pragma unroll
         for (int ks = 0; ks < BKV / 16; ++ks) {
-          const u32x4 a = tr_operand<BQ, false>(dSt[cur], 16 * ks, 32 * qb, lane);
-          const u32x4 bk = tr_operand<D, false>(Ks, 16 * ks, 32 * db, lane);
+          const u32x4 a = lds_tr16(sts + 16 * ks * BQ, s_off[bi][0], s_off[bi][1]);
+          const u32x4 bk = lds_tr16(Ks + 16 * ks * D, kt_off[bi][0], kt_off[bi][1]);
           acc = mfma32x32x16<T>(a, bk, acc);
         }
       }
       dqacc[bi] = acc;
     }
+  };
+
+  load_tile(0);
+  store_tile(IntC<0>{});
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(IntC<0>{}, t);
+    if (t + 1 < ntiles) step(IntC<1>{}, t + 1);
   }
   dq_atomics(q_begin + (ntiles - 1) * BQ);
 

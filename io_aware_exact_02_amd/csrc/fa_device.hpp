@@ -196,9 +196,65 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int k0, int n0
   return (u32x4){lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Value of lane (L ^ 32): exchange between the two 32-lane halves.
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// max(x, value of lane L^32): v_permlane32_swap exchanges the two 32-lane
+// halves, so the max of its two results is the pairwise max in every lane.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ------------------------------------------------------- hoisted LDS offsets
+//
+// Byte offsets (relative to a tile's base) that a lane uses for its MFMA
+// operand reads.  They depend on the lane only, so they are computed once
+// per kernel; inside the loops the tile base and the compile-time block
+// offsets become immediate offsets of the ds_read instructions.  The
+// swizzle has a period of 16 rows, so every block offset used below is a
+// multiple of 16 rows.
+
+// Row read of chunk (2*kc + hh) at row (rbase + l32), rbase a multiple of 32:
+// offset = rbase*2W + row_off<W>(lane, kc).
+template <int W>
+__device__ __forceinline__ uint32_t row_off(int lane, int kc) {
+  const int l32 = lane & 31, hh = lane >> 5;
+  return static_cast<uint32_t>(l32 * 2 * W + ((32 * kc) ^ (16 * (hh ^ swz<W>(l32)))));
+}
+
+// tr_operand read t (0, 1) for k0 = 0, n0 = 32*j: add k0*2W for other k0
+// (a multiple of 16).  SIGMA: rows stored under sigma_row.
+template <int W, bool SIGMA>
+__device__ __forceinline__ uint32_t tr_off(int lane, int t, int j) {
+  const int G = lane >> 4, s = lane & 15;
+  int r = 8 * (G >> 1) + (s >> 2) + 4 * t;
+  if constexpr (SIGMA) r = sigma32(r);
+  const int col = 16 * (G & 1) + 4 * (s & 3);
+  const int off = r * 2 * W + ((((col >> 3) ^ swz<W>(r)) << 4) | ((col & 7) << 1));
+  return static_cast<uint32_t>(off ^ (64 * j));
+}
+
+__device__ __forceinline__ u32x4 lds_ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + off);
+}
+__device__ __forceinline__ void lds_st16(void* base, uint32_t off, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(static_cast<char*>(base) + off) = v;
+}
+__device__ __forceinline__ u32x4 lds_tr16(const void* base, uint32_t off0, uint32_t off1) {
+  const u32x2 lo = lds_read_tr8(reinterpret_cast<const uint16_t*>(
+      static_cast<const char*>(base) + off0));
+  const u32x2 hi = lds_read_tr8(reinterpret_cast<const uint16_t*>(
+      static_cast<const char*>(base) + off1));
+  return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 }  // namespace fa

@@ -46,11 +46,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   constexpr int KC = D / 16;   // 16-wide k slices of Q K^T
   constexpr int NB = BC / 32;  // 32-key blocks per tile
   constexpr int DB = D / 32;   // 32-wide d blocks of O
+  constexpr int TILE = BC * D; // halves per K (or V) tile
 
   // Double-buffered K and V tiles, natural [key][d] layout, swizzled chunks;
   // K rows additionally stored under sigma_row.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -65,22 +66,49 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   const int h = bh % p.H;
   const int N = p.N;
 
-  const uint16_t* qbase = p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
-  const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
-
   const int q0 = qblk * BR + wave * 32;  // first query row of this wave
   const int qrow = q0 + l32;             // the query row this lane serves
 
   // B operand of S^T = K Q^T: q[qrow][16*kc + 8*hh + 0..7].
   u32x4 qreg[KC];
-  const uint32_t sign = p.negate_q ? 0x80008000u : 0u;
+  {
+    const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h + static_cast<int64_t>(qrow) * p.sq.n + 8 * hh;
+    const uint32_t sign = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (qrow < N) v = ldg16(qbase + static_cast<int64_t>(qrow) * p.sq.n + 16 * kc + 8 * hh);
-    qreg[kc] = v ^ sign;
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow < N) v = ldg16(qp + 16 * kc);
+      qreg[kc] = v ^ sign;
+    }
   }
+
+  // Per-lane LDS offsets, fixed for the whole kernel.
+  uint32_t k_off[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) k_off[kc] = row_off<D>(lane, kc);
+  uint32_t v_off[2][DB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) v_off[t][db] = tr_off<D, false>(lane, t, db);
+  // This thread's chunks of the K/V tile: global row/column and LDS offsets.
+  uint32_t st_k[NCH], st_v[NCH];
+  const uint16_t* kptr[NCH];
+  const uint16_t* vptr[NCH];
+  int ld_row[NCH];
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
+    const int c = tid + THREADS * it;
+    const int row = c / CPR;
+    const int col = (c % CPR) * 8;
+    ld_row[it] = row;
+    st_k[it] = 2 * tile_off<D>(sigma_row(row), col);
+    st_v[it] = 2 * tile_off<D>(row, col);
+    kptr[it] = p.k + b * p.sk.b + h * p.sk.h + static_cast<int64_t>(row) * p.sk.n + col;
+    vptr[it] = p.v + b * p.sv.b + h * p.sv.h + static_cast<int64_t>(row) * p.sv.n + col;
+  }
+  const int64_t k_step = static_cast<int64_t>(BC) * p.sk.n;
+  const int64_t v_step = static_cast<int64_t>(BC) * p.sv.n;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -88,139 +116,153 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   float m = -INFINITY;  // reference point (exp2 units) of this row's weights
   float l = 0.0f;       // sum of the fp32 weights exp2(t - m), this lane's keys
   float lb = 0.0f;      // sum of the same weights as rounded for the PV product
+  const float c_scale = p.c;
 
   const int qlast = min(qblk * BR + BR, N) - 1;
   const int ntiles = CAUSAL ? (qlast / BC + 1) : ((N + BC - 1) / BC);
 
   u32x4 pf_k[NCH], pf_v[NCH];
-  auto load_tile = [&](int kv0) {
+  // Load tile j (keys j*BC ..) into the staging registers.
+  auto load_tile = [&](int j) {
+    const int kv0 = j * BC;
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      const int c = tid + THREADS * it;
-      const int key = kv0 + c / CPR;
-      const int col = (c % CPR) * 8;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + col);
-        vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + col);
+      if (kv0 + ld_row[it] < N) {
+        kv = ldg16(kptr[it] + j * k_step);
+        vv = ldg16(vptr[it] + j * v_step);
       }
       pf_k[it] = kv;
       pf_v[it] = vv;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      const int c = tid + THREADS * it;
-      const int row = c / CPR;
-      const int col = (c % CPR) * 8;
-      lds_write16(&Ks[buf][tile_off<D>(sigma_row(row), col)], pf_k[it]);
-      lds_write16(&Vs[buf][tile_off<D>(row, col)], pf_v[it]);
+      lds_st16(Ks + BUF * TILE, st_k[it], pf_k[it]);
+      lds_st16(Vs + BUF * TILE, st_v[it], pf_v[it]);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int cur = j & 1;
-    const int kv0 = j * BC;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(kv0 + BC);
-
-    // Causal: tiles entirely above this wave's rows carry no weight for it.
-    if (!CAUSAL || kv0 <= q0 + 31) {
-      // S^T blocks: C value i of lane (l32, hh) is the score of query qrow
-      // against key kv0 + 32*nb + c_item(i, hh).
-      f32x16 sacc[NB];
+  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto compute = [&](auto bufc, auto maskc, int kv0) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASK = decltype(maskc)::value;
+    const uint16_t* kt = Ks + BUF * TILE;
+    const uint16_t* vt = Vs + BUF * TILE;
+    // C value i of lane (l32, hh) in block nb: query qrow, key
+    // kv0 + 32*nb + c_item(i, hh).
+    f32x16 sacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      sacc[nb] = (f32x16){};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4 a = lds_ld16(kt + 32 * nb * D, k_off[kc]);
+        sacc[nb] = mfma32x32x16<T>(a, qreg[kc], sacc[nb]);
+      }
+    }
+    if constexpr (MASK) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        sacc[nb] = (f32x16){};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const u32x4 a = lds_read16(&Ks[cur][tile_off<D>(32 * nb + l32, 16 * kc + 8 * hh)]);
-          sacc[nb] = mfma32x32x16<T>(a, qreg[kc], sacc[nb]);
-        }
-      }
-
-      const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
-      if (need_mask) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kv0 + 32 * nb + c_item(i, hh);
-            if (key >= N || (CAUSAL && key > qrow)) sacc[nb][i] = -INFINITY;
-          }
-        }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
-      }
-      mx = fmaxf(mx, xor32(mx));
-      // The reference point m only moves when the tile max exceeds it by more
-      // than 2^8 (in exp2 units); otherwise p <= 256 and nothing is rescaled.
-      // O = sum p v / sum p and LSE = m + log2(sum p) hold for any m, so this
-      // changes no result, only how often the accumulator is rescaled.
-      const float mt = mx * p.c;
-      if (__any(mt > m + 8.0f)) {
-        const float mnew = fmaxf(m, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        l *= alpha;
-        lb *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        m = mnew;
-      }
-
-      u32x4 pb[NB][2];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], p.c, -m));
-          l += pv[i];
-        }
-        pb[nb][0] = pack8<T>(pv);
-        pb[nb][1] = pack8<T>(pv + 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          lb = sum2_acc<T>(pb[nb][0][w], lb);
-          lb = sum2_acc<T>(pb[nb][1][w], lb);
-        }
-      }
-
-      // O^T += V^T P^T: A = V^T gathered transposed from the V tile, B = this
-      // lane's P values (keys 32*nb + 16*cc + 8*hh + 0..7).
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const u32x4 a = tr_operand<D, false>(Vs[cur], 32 * nb + 16 * cc, 32 * db, lane);
-            oacc[db] = mfma32x32x16<T>(a, pb[nb][cc], oacc[db]);
-          }
+          const int key = kv0 + 32 * nb + c_item(i, hh);
+          if (key >= N || (CAUSAL && key > qrow)) sacc[nb][i] = -INFINITY;
         }
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
+    }
+    mx = max_xor32(mx);
+    // The reference point m only moves when the tile max exceeds it by more
+    // than 2^8 (in exp2 units); otherwise p <= 256 and nothing is rescaled.
+    // O = sum p v / sum p and LSE = m + log2(sum p) hold for any m, so this
+    // changes no result, only how often the accumulator is rescaled.
+    const float mt = mx * c_scale;
+    if (__any(mt > m + 8.0f)) {
+      // Keeps this rarely taken block a real branch: without it the compiler
+      // if-converts it and rescales the accumulator on every tile.
+      asm volatile("" ::: "memory");
+      const float mnew = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+      lb *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m = mnew;
+    }
+    const float negm = -m;
+    u32x4 pb[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], c_scale, negm));
+        l += pv[i];
+      }
+      pb[nb][0] = pack8<T>(pv);
+      pb[nb][1] = pack8<T>(pv + 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lb = sum2_acc<T>(pb[nb][0][w], lb);
+        lb = sum2_acc<T>(pb[nb][1][w], lb);
+      }
+    }
+    // O^T += V^T P^T: A = V^T gathered transposed from the V tile (keys
+    // 32*nb + 16*cc + 8*hh + 0..7), B = this lane's P values for those keys.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const uint16_t* vk = vt + (32 * nb + 16 * cc) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 a = lds_tr16(vk, v_off[0][db], v_off[1][db]);
+          oacc[db] = mfma32x32x16<T>(a, pb[nb][cc], oacc[db]);
+        }
+      }
+    }
+  };
 
-    if (has_next) store_tile(cur ^ 1);
+  auto step = [&](auto bufc, int j) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int kv0 = j * BC;
+    const bool has_next = j + 1 < ntiles;
+    if (has_next) load_tile(j + 1);
+    // Causal: tiles entirely above this wave's rows carry no weight for it.
+    if (!CAUSAL || kv0 <= q0 + 31) {
+      const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
+      if (need_mask) {
+        compute(bufc, IntC<1>{}, kv0);
+      } else {
+        compute(bufc, IntC<0>{}, kv0);
+      }
+    }
+    if (has_next) store_tile(IntC<BUF ^ 1>{});
     __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(IntC<0>{});
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    step(IntC<0>{}, j);
+    if (j + 1 < ntiles) step(IntC<1>{}, j + 1);
   }
 
   // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
   // O is normalised by the sum of the weights exactly as the PV product used
   // them (rounded to the input type), so each output row is a convex
   // combination of V rows; the LSE uses the unrounded fp32 sum.
-  const float lt = l + xor32(l);
-  const float inv = __builtin_amdgcn_rcpf(lb + xor32(lb));
+  const float lt = sum_xor32(l);
+  const float inv = __builtin_amdgcn_rcpf(sum_xor32(lb));
   if (qrow < N) {
     uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
 #pragma unroll
