@@ -70,6 +70,10 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # Loading resolves every symbol: a kernel whose host launch stub was not
+    # emitted fails here, not at the first call.
+    import ctypes
+    ctypes.CDLL(tmp)
     os.replace(tmp, LIB)
     return LIB
 

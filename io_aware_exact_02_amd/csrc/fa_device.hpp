@@ -28,6 +28,9 @@ struct F16 {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate that waits for vmcnt == 0 only (expcnt and lgkmcnt at
+// their maxima): vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14.
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 constexpr float kLn2 = 0.6931471805599453f;
 
 // v_mfma_f32_32x32x16_{bf16,f16}: C[32x32] += A[32x16] * B[16x32].
@@ -250,6 +253,15 @@ __device__ __forceinline__ u32x4 lds_tr16(const void* base, uint32_t off0, uint3
   const u32x2 hi = lds_read_tr8(reinterpret_cast<const uint16_t*>(
       static_cast<const char*>(base) + off1));
   return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane i
+// writes LDS bytes [ldst + 16*i, ldst + 16*i + 16); ldst must be the same in
+// every lane.  Completion is tracked by vmcnt.  Kept as a plain (non-template)
+// function: referenced from inside kernel templates directly, the builtin
+// makes the host compilation pass drop those kernels' launch stubs.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
 
 template <int V>

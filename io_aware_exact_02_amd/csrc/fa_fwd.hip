@@ -38,8 +38,12 @@ struct FwdCfg {
   static_assert(NCH * THREADS == BC * CPR, "tile load must divide evenly");
 };
 
+// Occupancy target: 4 waves per SIMD for 8-wave workgroups (128 VGPRs; the
+// forward is bound by its softmax VALU work and needs waves to overlap it
+// with the matrix cores), 2 for 4-wave workgroups.
 template <typename T, int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : 2)))
+void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D, NW>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, THREADS = Cfg::THREADS;
   constexpr int CPR = Cfg::CPR, NCH = Cfg::NCH;
@@ -91,24 +95,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < DB; ++db) v_off[t][db] = tr_off<D, false>(lane, t, db);
-  // This thread's chunks of the K/V tile: global row/column and LDS offsets.
-  uint32_t st_k[NCH], st_v[NCH];
-  const uint16_t* kptr[NCH];
-  const uint16_t* vptr[NCH];
-  int ld_row[NCH];
+  // Direct global -> LDS tile loads: one global_load_lds_dwordx4 fills 1 KB
+  // of a tile, lane i writing the 16-byte slot i.  Each lane therefore
+  // fetches the global chunk that belongs in its slot under the tile's
+  // layout (swizzled chunks; sigma_row for K).  Offsets in elements, within
+  // a tile of BC rows.
+  uint32_t gk_off[NCH], gv_off[NCH];
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
-    const int c = tid + THREADS * it;
-    const int row = c / CPR;
-    const int col = (c % CPR) * 8;
-    ld_row[it] = row;
-    st_k[it] = 2 * tile_off<D>(sigma_row(row), col);
-    st_v[it] = 2 * tile_off<D>(row, col);
-    kptr[it] = p.k + b * p.sk.b + h * p.sk.h + static_cast<int64_t>(row) * p.sk.n + col;
-    vptr[it] = p.v + b * p.sv.b + h * p.sv.h + static_cast<int64_t>(row) * p.sv.n + col;
+    const int slot = (wave + NW * it) * 64 + lane;
+    const int pr = slot / CPR;                            // stored row
+    const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;      // logical column
+    gk_off[it] = static_cast<uint32_t>(sigma_row(pr) * p.sk.n + col);
+    gv_off[it] = static_cast<uint32_t>(pr * p.sv.n + col);
   }
-  const int64_t k_step = static_cast<int64_t>(BC) * p.sk.n;
-  const int64_t v_step = static_cast<int64_t>(BC) * p.sv.n;
+  const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
+  const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -121,28 +123,34 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   const int qlast = min(qblk * BR + BR, N) - 1;
   const int ntiles = CAUSAL ? (qlast / BC + 1) : ((N + BC - 1) / BC);
 
-  u32x4 pf_k[NCH], pf_v[NCH];
-  // Load tile j (keys j*BC ..) into the staging registers.
-  auto load_tile = [&](int j) {
+  // Issue the loads of tile j into buffer BUF.  Rows past N (last tile only)
+  // are clamped to row N-1: those keys are masked, so their finite values
+  // never reach the result.
+  auto load_tile = [&](auto bufc, int j) {
+    constexpr int BUF = decltype(bufc)::value;
     const int kv0 = j * BC;
+    const uint16_t* kt = kbase + static_cast<int64_t>(kv0) * p.sk.n;
+    const uint16_t* vt = vbase + static_cast<int64_t>(kv0) * p.sv.n;
+    const bool tail = kv0 + BC > N;
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (kv0 + ld_row[it] < N) {
-        kv = ldg16(kptr[it] + j * k_step);
-        vv = ldg16(vptr[it] + j * v_step);
+      uint32_t ko = gk_off[it], vo = gv_off[it];
+      if (tail) {
+        const int last = N - 1 - kv0;
+        const int slot = (wave + NW * it) * 64 + lane;
+        const int pr = slot / CPR;
+        const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;
+        ko = static_cast<uint32_t>(min(sigma_row(pr), last) * p.sk.n + col);
+        vo = static_cast<uint32_t>(min(pr, last) * p.sv.n + col);
       }
-      pf_k[it] = kv;
-      pf_v[it] = vv;
+      lds_dma16(kt + ko, Ks + BUF * TILE + (wave + NW * it) * 512);
+      lds_dma16(vt + vo, Vs + BUF * TILE + (wave + NW * it) * 512);
     }
   };
-  auto store_tile = [&](auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-#pragma unroll
-    for (int it = 0; it < NCH; ++it) {
-      lds_st16(Ks + BUF * TILE, st_k[it], pf_k[it]);
-      lds_st16(Vs + BUF * TILE, st_v[it], pf_v[it]);
-    }
+  // Wait for this wave's tile loads, then for every wave's.
+  auto tile_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
   };
 
   // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
@@ -234,8 +242,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
   auto step = [&](auto bufc, int j) {
     constexpr int BUF = decltype(bufc)::value;
     const int kv0 = j * BC;
-    const bool has_next = j + 1 < ntiles;
-    if (has_next) load_tile(j + 1);
+    if (j + 1 < ntiles) load_tile(IntC<BUF ^ 1>{}, j + 1);
     // Causal: tiles entirely above this wave's rows carry no weight for it.
     if (!CAUSAL || kv0 <= q0 + 31) {
       const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
@@ -245,13 +252,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdParams p) {
         compute(bufc, IntC<0>{}, kv0);
       }
     }
-    if (has_next) store_tile(IntC<BUF ^ 1>{});
-    __syncthreads();
+    tile_barrier();
   };
 
-  load_tile(0);
-  store_tile(IntC<0>{});
-  __syncthreads();
+  load_tile(IntC<0>{}, 0);
+  tile_barrier();
   for (int j = 0; j < ntiles; j += 2) {
     step(IntC<0>{}, j);
     if (j + 1 < ntiles) step(IntC<1>{}, j + 1);
