@@ -38,11 +38,19 @@ struct FwdCfg {
   static_assert(NCH * THREADS == BC * CPR, "tile load must divide evenly");
 };
 
-// Occupancy target: 4 waves per SIMD for 8-wave workgroups (128 VGPRs; the
-// forward is bound by its softmax VALU work and needs waves to overlap it
-// with the matrix cores), 2 for 4-wave workgroups.
+// Occupancy target in waves per SIMD.  The head_dim-64 forward is bound by
+// its softmax VALU work and needs several waves to overlap it with the
+// matrix cores, so the causal 8-wave kernel targets 4 waves (128 VGPRs).
+// Every other instantiation takes the highest target that compiles without
+// spilling (the non-causal kernels hold more live registers).
+template <int D, int NW, bool CAUSAL>
+struct FwdOccupancy {
+  static constexpr int value = D == 64 ? (NW == 8 && CAUSAL ? 4 : 2) : (CAUSAL ? 2 : 1);
+};
+
 template <typename T, int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 4 : 2)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(FwdOccupancy<D, NW, CAUSAL>::value)))
 void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D, NW>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, THREADS = Cfg::THREADS;
@@ -297,11 +305,15 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
 }
 
 // 8 waves (256 query rows) per workgroup when that still gives at least two
-// workgroups per compute unit, else 4 waves (128 rows).
+// workgroups per compute unit, else 4 waves (128 rows).  The non-causal
+// head_dim-128 kernel always uses 4 waves: at 8 it would not fit its
+// registers into the two waves per SIMD an 8-wave workgroup needs.
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
-  if (wg8 >= 512) return launch_fwd_nw<T, D, 8, CAUSAL>(p, s);
+  if constexpr (D == 64 || CAUSAL) {
+    const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
+    if (wg8 >= 512) return launch_fwd_nw<T, D, 8, CAUSAL>(p, s);
+  }
   return launch_fwd_nw<T, D, 4, CAUSAL>(p, s);
 }
 
