@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 // load ever waits behind them.  Q, dO, LSE and Dvec of the next tile are
 // prefetched into registers during the current one (LDS double buffer, one
 // barrier per tile).
-template <int D, int NW>
+template <int D, int NW, int BQ_>
 struct BwdCfg {
   static constexpr int BKV = 32 * NW;   // keys per workgroup
-  static constexpr int BQ = 64;         // query rows per tile
+  static constexpr int BQ = BQ_;        // query rows per tile (32 or 64)
   static constexpr int NQB = BQ / 32;   // 32-row query blocks per tile
   static constexpr int DB = D / 32;     // 32-wide d blocks
   static constexpr int NBLK = NQB * DB; // 32x32 dQ blocks per tile
@@ -79,9 +79,9 @@ struct BwdCfg {
   static_assert(QPT * THREADS == BQ * CPR, "tile load must divide evenly");
 };
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, int BQ_, bool KLDS, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
-  using Cfg = BwdCfg<D, NW>;
+  using Cfg = BwdCfg<D, NW, BQ_>;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NQB = Cfg::NQB, DB = Cfg::DB;
   constexpr int NBLK = Cfg::NBLK, BPW = Cfg::BPW, THREADS = Cfg::THREADS;
   constexpr int CPR = Cfg::CPR, QPT = Cfg::QPT;
@@ -121,15 +121,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int key = kw0 + l32;  // the key this lane serves in S and dP
 
   // B operands of S = Q K^T and dP = dO V^T: k / v[key][16*kc + 8*hh + 0..7].
-  u32x4 kreg[KC], vreg[KC];
+  // With KLDS the K operand is read from the workgroup's K rows in LDS
+  // instead (register budget at head_dim 128).
+  u32x4 kreg[KLDS ? 1 : KC], vreg[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
     if (key < N) {
-      kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + 16 * kc + 8 * hh);
+      if constexpr (!KLDS) kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + 16 * kc + 8 * hh);
       vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + 16 * kc + 8 * hh);
     }
-    kreg[kc] = kv;
+    if constexpr (!KLDS) kreg[kc] = kv;
     vreg[kc] = vv;
   }
   // The workgroup's K rows in LDS (B operand of dQ = dS K).
@@ -274,7 +276,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s = (f32x16){};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32x32x16<T>(lds_ld16(qs + 32 * qb * D, q_off[kc]), kreg[kc], s);
+        u32x4 kop;
+        if constexpr (KLDS) {
+          kop = lds_ld16(Ks + 32 * wave * D, q_off[kc]);  // rows of this wave's keys
+        } else {
+          kop = kreg[kc];
+        }
+        s = mfma32x32x16<T>(lds_ld16(qs + 32 * qb * D, q_off[kc]), kop, s);
         dp = mfma32x32x16<T>(lds_ld16(dos + 32 * qb * D, q_off[kc]), vreg[kc], dp);
       }
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * qb);
@@ -390,11 +398,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-// Waves per workgroup of the dK/dV kernel: 8 at head_dim 64 (256 keys per
-// workgroup halves the dQ atomics), 4 at head_dim 128 (register budget).
+// dK/dV kernel shape per head_dim.  Keys per workgroup (32 per wave) set the
+// number of dQ atomics: each dQ element receives one per key block.  At
+// head_dim 64, 8 waves (256 keys) fit in 256 registers per wave; at head_dim
+// 128 the dK/dV accumulators of 4 waves (128 keys) already take half of them.
 template <int D>
-struct BwdWaves {
+struct BwdShape {
   static constexpr int NW = D == 64 ? 8 : 4;
+  static constexpr int BQ = 64;
+  static constexpr bool KLDS = false;
 };
 
 // ------------------------------------------------------------------ kernel 3
@@ -419,9 +431,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream_t s) {
-  constexpr int NW = BwdWaves<D>::NW;
+  using Sh = BwdShape<D>;
+  constexpr int NW = Sh::NW;
   BwdParams p = p_in;
-  p.num_kblocks = (p.N + BwdCfg<D, NW>::BKV - 1) / BwdCfg<D, NW>::BKV;
+  p.num_kblocks = (p.N + BwdCfg<D, NW, Sh::BQ>::BKV - 1) / BwdCfg<D, NW, Sh::BQ>::BKV;
   const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
   constexpr int RPB = 256 / (D / 8);
   const unsigned row_blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
@@ -432,8 +445,8 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   }
   if (stages & 2u) {
     const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * NW), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4u) {

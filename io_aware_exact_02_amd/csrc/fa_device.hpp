@@ -140,19 +140,22 @@ __device__ __forceinline__ int sigma_row(int r) { return (r & ~31) | sigma32(r &
 
 // ---------------------------------------------------------------- LDS tiles
 //
-// Tiles are stored row-major with W halves per row (W = 64 or 128, no
+// Tiles are stored row-major with W halves per row (W = 32, 64 or 128, no
 // padding) and the 16-byte chunks of each row XOR-swizzled by a function of
 // the row.  The swizzle keeps two access patterns free of bank conflicts on
 // the 64-bank LDS:
 //   * row reads (ds_read_b128): 16 consecutive rows, same logical chunk;
 //   * transposed reads (ds_read_b64_tr_b16): 4 consecutive rows starting at
 //     a multiple of 4, an aligned block of 4 logical chunks.
+// W = 32 (4 chunks, four rows per 256-byte bank line): g(r) = r/4 % 4.
 // W = 64 (8 chunks, two rows per 256-byte bank line): g(r) = bitrev3(r/2 % 8).
 // W = 128 (16 chunks, one row per bank line): g(r) = bitrev4(r % 16).
 template <int W>
 __device__ __forceinline__ int swz(int r) {
-  static_assert(W == 64 || W == 128, "tile width");
-  if constexpr (W == 64) {
+  static_assert(W == 32 || W == 64 || W == 128, "tile width");
+  if constexpr (W == 32) {
+    return (r >> 2) & 3;
+  } else if constexpr (W == 64) {
     const int u = (r >> 1) & 7;
     return ((u & 1) << 2) | (u & 2) | ((u >> 2) & 1);
   } else {

@@ -3,8 +3,9 @@
 // One kernel computes O = softmax(scale * Q K^T) V for a block of query rows
 // without ever writing S or P to memory: K/V tiles are staged through LDS,
 // both products run on the matrix cores, and the softmax is carried online
-// with a running row maximum m and normaliser l (the tiling / online-softmax
-// scheme of the pwwt.cn page, section "2. 分块处理").  The output accumulator
+// with a per-row reference point m and normaliser l (the tiling / online-
+// softmax scheme of the pwwt.cn page, section "2. 分块处理"; m follows the
+// row maximum lazily, see soft_half).  The output accumulator
 // is kept unscaled and divided by l once at the end, and only the row
 // logsumexp is stored for the backward pass (hotelren.com FlashAttention-2
 // walkthrough, section 3.1; its printed recurrence is garbled, the form used
@@ -21,8 +22,8 @@
 // the B operand of the next product O^T += V^T P^T, with no data movement;
 // that product's A operand V^T is gathered from the natural-layout V tile by
 // transposing LDS reads.  K/V tiles of 64 keys are double-buffered: the next
-// tile is loaded into registers while the current one is consumed, so there
-// is one barrier per tile.
+// tile is copied global -> LDS asynchronously while the current one is
+// consumed, so there is one barrier per tile.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -61,9 +62,14 @@ void fwd_kernel(FwdParams p) {
   constexpr int TILE = BC * D; // halves per K (or V) tile
 
   // Double-buffered K and V tiles, natural [key][d] layout, swizzled chunks;
-  // K rows additionally stored under sigma_row.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * TILE];
+  // K rows additionally stored under sigma_row.  Each buffer is its own LDS
+  // object: the compiler then sees that the asynchronous loads into one
+  // buffer cannot alias reads of the other and does not wait for them before
+  // the current tile's reads.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[TILE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -151,8 +157,8 @@ void fwd_kernel(FwdParams p) {
         ko = static_cast<uint32_t>(min(sigma_row(pr), last) * p.sk.n + col);
         vo = static_cast<uint32_t>(min(pr, last) * p.sv.n + col);
       }
-      lds_dma16(kt + ko, Ks + BUF * TILE + (wave + NW * it) * 512);
-      lds_dma16(vt + vo, Vs + BUF * TILE + (wave + NW * it) * 512);
+      lds_dma16(kt + ko, (BUF ? Ks1 : Ks0) + (wave + NW * it) * 512);
+      lds_dma16(vt + vo, (BUF ? Vs1 : Vs0) + (wave + NW * it) * 512);
     }
   };
   // Wait for this wave's tile loads, then for every wave's.
@@ -161,90 +167,107 @@ void fwd_kernel(FwdParams p) {
     __syncthreads();
   };
 
-  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T, taken as two
+  // 32-key halves so that the softmax of the first half can overlap the
+  // second half's S product and the second softmax the first PV product.
   auto compute = [&](auto bufc, auto maskc, int kv0) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASK = decltype(maskc)::value;
-    const uint16_t* kt = Ks + BUF * TILE;
-    const uint16_t* vt = Vs + BUF * TILE;
-    // C value i of lane (l32, hh) in block nb: query qrow, key
+    static_assert(NB == 2, "two 32-key halves per tile");
+    const uint16_t* kt = BUF ? Ks1 : Ks0;
+    const uint16_t* vt = BUF ? Vs1 : Vs0;
+    // S^T of half nb.  C value i of lane (l32, hh): query qrow, key
     // kv0 + 32*nb + c_item(i, hh).
-    f32x16 sacc[NB];
+    auto s_half = [&](int nb) {
+      f32x16 acc = (f32x16){};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      sacc[nb] = (f32x16){};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 a = lds_ld16(kt + 32 * nb * D, k_off[kc]);
-        sacc[nb] = mfma32x32x16<T>(a, qreg[kc], sacc[nb]);
-      }
-    }
-    if constexpr (MASK) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+      for (int kc = 0; kc < KC; ++kc)
+        acc = mfma32x32x16<T>(lds_ld16(kt + 32 * nb * D, k_off[kc]), qreg[kc], acc);
+      return acc;
+    };
+    auto mask_half = [&](f32x16& acc, int nb) {
+      if constexpr (MASK) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * nb + c_item(i, hh);
-          if (key >= N || (CAUSAL && key > qrow)) sacc[nb][i] = -INFINITY;
+          if (key >= N || (CAUSAL && key > qrow)) acc[i] = -INFINITY;
         }
       }
-    }
-    float mx = -INFINITY;
+    };
+    // Weights of one half, p = exp2(c*s - m), as MFMA operands.  They are
+    // computed against the current reference point m; m only moves when that
+    // makes this lane's sum over the half exceed 2^8 (or on the first tile,
+    // where m is -inf and the sum is not finite): then m becomes the running
+    // row max, the accumulators are rescaled and the weights recomputed.  So
+    // every weight stays below 2^8 and the row max is only taken when m
+    // moves.  O = sum p v / sum p and LSE = m + log2(sum p) hold for any m:
+    // this changes no result, only how often the accumulators are rescaled.
+    auto soft_half = [&](const f32x16& acc, u32x4 (&pbh)[2]) {
+      float lt, lbt;
+      auto weights = [&]() {
+        const float negm = -m;
+        float pv[16];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c_scale, negm));
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
-    }
-    mx = max_xor32(mx);
-    // The reference point m only moves when the tile max exceeds it by more
-    // than 2^8 (in exp2 units); otherwise p <= 256 and nothing is rescaled.
-    // O = sum p v / sum p and LSE = m + log2(sum p) hold for any m, so this
-    // changes no result, only how often the accumulator is rescaled.
-    const float mt = mx * c_scale;
-    if (__any(mt > m + 8.0f)) {
-      // Keeps this rarely taken block a real branch: without it the compiler
-      // if-converts it and rescales the accumulator on every tile.
-      asm volatile("" ::: "memory");
-      const float mnew = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
-      lb *= alpha;
+        for (int i = 0; i < 16; i += 2) {
+          s0 += pv[i];
+          s1 += pv[i + 1];
+        }
+        lt = s0 + s1;
+        pbh[0] = pack8<T>(pv);
+        pbh[1] = pack8<T>(pv + 8);
+        lbt = 0.0f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m = mnew;
-    }
-    const float negm = -m;
-    u32x4 pb[NB][2];
+        for (int w = 0; w < 4; ++w) {
+          lbt = sum2_acc<T>(pbh[0][w], lbt);
+          lbt = sum2_acc<T>(pbh[1][w], lbt);
+        }
+      };
+      weights();
+      if (__any(!(lt <= 256.0f))) {
+        // Keeps this rarely taken block a real branch: without it the
+        // compiler if-converts it and rescales the accumulator every time.
+        asm volatile("" ::: "memory");
+        float mx0 = acc[0], mx1 = acc[1];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float pv[16];
+        for (int i = 0; i < 16; i += 2) {
+          mx0 = fmaxf(mx0, acc[i]);
+          mx1 = fmaxf(mx1, acc[i + 1]);
+        }
+        const float mnew = fmaxf(m, max_xor32(fmaxf(mx0, mx1)) * c_scale);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        l *= alpha;
+        lb *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[nb][i], c_scale, negm));
-        l += pv[i];
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m = mnew;
+        weights();
       }
-      pb[nb][0] = pack8<T>(pv);
-      pb[nb][1] = pack8<T>(pv + 8);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        lb = sum2_acc<T>(pb[nb][0][w], lb);
-        lb = sum2_acc<T>(pb[nb][1][w], lb);
-      }
-    }
-    // O^T += V^T P^T: A = V^T gathered transposed from the V tile (keys
-    // 32*nb + 16*cc + 8*hh + 0..7), B = this lane's P values for those keys.
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+      l += lt;
+      lb += lbt;
+    };
+    // O^T += V^T P^T for half nb: A = V^T gathered transposed from the V
+    // tile (keys 32*nb + 16*cc + 8*hh + 0..7), B = this lane's weights.
+    auto pv_half = [&](const u32x4 (&pbh)[2], int nb) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const uint16_t* vk = vt + (32 * nb + 16 * cc) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 a = lds_tr16(vk, v_off[0][db], v_off[1][db]);
-          oacc[db] = mfma32x32x16<T>(a, pb[nb][cc], oacc[db]);
-        }
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = mfma32x32x16<T>(lds_tr16(vk, v_off[0][db], v_off[1][db]), pbh[cc], oacc[db]);
       }
-    }
+    };
+    f32x16 s0 = s_half(0);
+    mask_half(s0, 0);
+    f32x16 s1 = s_half(1);
+    u32x4 p0[2], p1[2];
+    soft_half(s0, p0);
+    mask_half(s1, 1);
+    pv_half(p0, 0);
+    soft_half(s1, p1);
+    pv_half(p1, 1);
   };
 
   auto step = [&](auto bufc, int j) {
