@@ -18,7 +18,7 @@
  *   The library never synchronises; kernel faults surface at the caller's
  *   next synchronisation, as usual in HIP.
  * - Element type of q, k, v, o, dout, dq, dk, dv: `dtype` (FA_F16 or
- *   FA_BF16).  lse and the workspace are fp32.
+ *   FA_BF16).  lse is fp32; the workspace layout is given below.
  * - Tensor layout: logical [B, N, H, D] (batch, sequence, head, head_dim),
  *   the flash_attn_func layout of the hotelren.com walkthrough, section 5.
  *   Element strides (b, n, h) per tensor are given by the optional strides
@@ -89,10 +89,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const fa_fwd_strides* strides, hipStream_t stream);
 
 /*
- * fa_bwd_workspace_bytes -- size of the fp32 scratch fa_bwd needs:
- * the row vector Dvec = rowsum(dO o O) [B, H, N] and the dQ accumulator
- * [B, H, N, D], each rounded up to 256 bytes.  O(N*D) per head; no N*N term.
- * Returns 0 for invalid sizes.
+ * fa_bwd_workspace_bytes -- size of the scratch fa_bwd needs: the row vector
+ * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
+ * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]
+ * (fp32) and one dQ bound per head [B*H] (fp32), each part rounded
+ * up to 256 bytes.  O(N*D) per head; no N*N term.  Returns 0 for invalid
+ * sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 
@@ -109,8 +111,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
  *                     fa_bwd_workspace_bytes(B, H, N, D) bytes, 256-byte
  *                     aligned; contents undefined on entry and on exit.
  * Three kernels are enqueued on `stream`: the Dvec preprocess (which also
- * clears the dQ accumulator), the K/V-block-parallel dK/dV kernel that
- * accumulates dQ with fp32 atomics, and the dQ conversion.
+ * clears the dQ accumulator and takes the largest |dO|, |K| and |V|
+ * elements per head), the K/V-block-parallel dK/dV kernel that accumulates
+ * dQ with 32-bit integer atomics in units of B / 2^30, B = 4 D max|dO|
+ * max|K| max|V| per (batch, head) -- a bound on any partial sum of dS K
+ * -- and the dQ conversion.  The integer sum is exact, so dq is bitwise
+ * reproducible; each key block's contribution is rounded to the nearest
+ * unit.  Heads whose bound is not a finite normal float get dq = 0.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -121,9 +128,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 /*
  * fa_bwd_stages -- fa_bwd split into its three kernels, for callers that
  * schedule or time them separately.  Arguments are those of fa_bwd; `stages`
- * is a bit mask: FA_STAGE_PREPROCESS (Dvec and the cleared dQ accumulator,
- * written to the workspace), FA_STAGE_DKDV (dK, dV, and dQ accumulated in
- * the workspace) and FA_STAGE_DQ (dq from the accumulator).  Each stage
+ * is a bit mask: FA_STAGE_PREPROCESS (Dvec, the cleared dQ accumulator and
+ * the bound maxima, written to the workspace), FA_STAGE_DKDV (dK, dV, and dQ
+ * accumulated in the workspace) and FA_STAGE_DQ (dq from the accumulator).  Each stage
  * reads what the previous one left in the same workspace, so the stages must
  * run in this order on one stream with the same workspace; fa_bwd is
  * fa_bwd_stages with all three bits.  stages = 0 or unknown bits:

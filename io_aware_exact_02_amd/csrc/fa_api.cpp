@@ -87,10 +87,29 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+namespace {
+// Workspace layout of fa_bwd, each part starting on a 256-byte boundary:
+// Dvec [B, H, N] fp32 | dQ accumulator [B, H, N, D] int32 | bound maxima
+// [B*H, 3, ceil(N / 16)] fp32 | dQ bound [B*H] fp32.
+struct BwdWorkspace {
+  size_t dvec, dq, part, unit, total;
+};
+BwdWorkspace bwd_workspace(int B, int H, int N, int D) {
+  const size_t heads = static_cast<size_t>(B) * H;
+  const size_t rows = heads * N;
+  BwdWorkspace w{};
+  w.dvec = 0;
+  w.dq = align256(rows * sizeof(float));
+  w.part = w.dq + align256(rows * D * sizeof(int32_t));
+  w.unit = w.part + align256(heads * 3 * ((static_cast<size_t>(N) + 15) / 16) * sizeof(float));
+  w.total = w.unit + align256(heads * sizeof(float));
+  return w;
+}
+}  // namespace
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D) {
   if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return 0;
-  const size_t rows = static_cast<size_t>(B) * H * N;
-  return align256(rows * sizeof(float)) + align256(rows * D * sizeof(float));
+  return bwd_workspace(B, H, N, D).total;
 }
 
 int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
@@ -136,10 +155,12 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
     st = check_strides(*s, B, N, H, D);
     if (st != FA_OK) return st;
   }
-  const size_t rows = static_cast<size_t>(B) * H * N;
-  p.dvec = static_cast<float*>(workspace);
-  p.dq_accum = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align256(rows * sizeof(float)));
+  const BwdWorkspace w = bwd_workspace(B, H, N, D);
+  char* ws = static_cast<char*>(workspace);
+  p.dvec = reinterpret_cast<float*>(ws + w.dvec);
+  p.dq_fix = reinterpret_cast<int32_t*>(ws + w.dq);
+  p.bound_part = reinterpret_cast<float*>(ws + w.part);
+  p.dq_bound = reinterpret_cast<float*>(ws + w.unit);
   p.B = B;
   p.H = H;
   p.N = N;

@@ -10,41 +10,93 @@
 //   dQ = scale dS K,   where Dvec_i = rowsum(dO_i o O_i).
 //
 // Three kernels:
-//   1. preprocess: Dvec = rowsum(dO o O) and zero the fp32 dQ accumulator;
+//   1. preprocess: Dvec = rowsum(dO o O), clear the dQ accumulator, and the
+//      per-block maxima of |dO|, |K| and |V| elements that bound dQ;
 //   2. dK/dV: one workgroup per block of keys (parallel over key blocks,
 //      batch and heads), K/V of its keys resident in registers, looping over
-//      query tiles; dQ contributions go to the fp32 accumulator with atomics;
+//      query tiles; dQ contributions are added to the accumulator with
+//      integer atomics (fixed point, see below);
 //   3. dQ conversion: scale, round to the input type, strided store.
+//
+// dQ accumulator.  Each dQ element receives one partial sum per key block,
+// from different workgroups, so the sum needs device-wide atomics; on this
+// chip those execute at the memory side and bound the whole backward.
+// 32-bit integer adds run there about 1.3x faster than fp32 adds, so the
+// accumulator is fixed point: one unit is B / 2^30, with B a bound on
+// |sum_j dS_ij K_jd| over any subset of keys.  From dS_ij = P_ij (dP_ij -
+// Dvec_i), sum_j P_ij = 1, |dP_ij| = |dO_i . V_j| <= D max|dO| max|V| and
+// |Dvec_i| = |dO_i . O_i| <= D max|dO| max|V| (O_i is a convex combination
+// of the V_j), with element-wise maxima over the head:
+//   B = 4 D max|dO| max|K| max|V|   (2x margin for rounding),
+// per (batch, head).  Element-wise maxima, not norms: squares of tiny or
+// huge inputs would under- or overflow.  Every partial sum is rounded to the nearest unit; the
+// total stays within 2^30 units, so the 32-bit sum is exact whatever the
+// order of the adds -- dQ is deterministic -- and its error is at most half
+// a unit per key block.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 
 // ------------------------------------------------------------------ kernel 1
+// Grid (ceil(N / RPB), B*H): each workgroup covers RPB rows of one head and
+// records the largest |dO|, |K| and |V| elements of those rows.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   constexpr int TPR = D / 8;       // threads per row (8 elements each)
   constexpr int RPB = 256 / TPR;   // rows per workgroup
   const int tid = threadIdx.x;
   const int part = tid % TPR;
-  const int64_t total = static_cast<int64_t>(p.B) * p.H * p.N;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + tid / TPR;
-  float s = 0.0f;
-  if (row < total) {
-    const int n = static_cast<int>(row % p.N);
-    const int bh = static_cast<int>(row / p.N);
-    const int b = bh / p.H, h = bh % p.H;
-    const u32x4 o = ldg16(p.o + b * p.so.b + static_cast<int64_t>(n) * p.so.n + h * p.so.h + part * 8);
-    const u32x4 d = ldg16(p.dout + b * p.sdo.b + static_cast<int64_t>(n) * p.sdo.n + h * p.sdo.h + part * 8);
+  const int bh = blockIdx.y;
+  const int b = bh / p.H, h = bh % p.H;
+  const int n = static_cast<int>(blockIdx.x) * RPB + tid / TPR;
+  const int64_t row = static_cast<int64_t>(bh) * p.N + n;
+  float s = 0.0f, domax = 0.0f, vmax = 0.0f, kmax = 0.0f;
+  if (n < p.N) {
+    const int64_t nn = n;
+    const u32x4 o = ldg16(p.o + b * p.so.b + nn * p.so.n + h * p.so.h + part * 8);
+    const u32x4 d = ldg16(p.dout + b * p.sdo.b + nn * p.sdo.n + h * p.sdo.h + part * 8);
+    const u32x4 k = ldg16(p.k + b * p.sk.b + nn * p.sk.n + h * p.sk.h + part * 8);
+    const u32x4 v = ldg16(p.v + b * p.sv.b + nn * p.sv.n + h * p.sv.h + part * 8);
     s = dot8<T>(o, d);
-    float* acc = p.dq_accum + row * D + part * 8;
+    domax = absmax8<T>(d);
+    vmax = absmax8<T>(v);
+    kmax = absmax8<T>(k);
+    int32_t* acc = p.dq_fix + row * D + part * 8;
     const u32x4 z = {0u, 0u, 0u, 0u};
     stg16(acc, z);
     stg16(acc + 4, z);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (row < total && part == 0) p.dvec[row] = s;
+  if (n < p.N && part == 0) p.dvec[row] = s;
+  // Maxima over the workgroup's rows: across the wave, then the four waves.
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    domax = fmaxf(domax, __shfl_xor(domax, off, 64));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
+  }
+  __shared__ float red[4][3];
+  if ((tid & 63) == 0) {
+    red[tid >> 6][0] = domax;
+    red[tid >> 6][1] = kmax;
+    red[tid >> 6][2] = vmax;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m0 = red[0][0], m1 = red[0][1], m2 = red[0][2];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      m0 = fmaxf(m0, red[w][0]);
+      m1 = fmaxf(m1, red[w][1]);
+      m2 = fmaxf(m2, red[w][2]);
+    }
+    float* out = p.bound_part + static_cast<int64_t>(bh) * 3 * p.npart + blockIdx.x;
+    out[0] = m0;
+    out[p.npart] = m1;
+    out[2 * p.npart] = m2;
+  }
 }
 
 // ------------------------------------------------------------------ kernel 2
@@ -114,7 +166,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
   const float* lse_row = p.lse + static_cast<int64_t>(bh) * N;
   const float* dvec_row = p.dvec + static_cast<int64_t>(bh) * N;
-  float* dq_acc = p.dq_accum + static_cast<int64_t>(bh) * N * D;
+  int32_t* dq_acc = p.dq_fix + static_cast<int64_t>(bh) * N * D;
 
   const int kb0 = kblk * BKV;
   const int kw0 = kb0 + 32 * wave;
@@ -134,6 +186,45 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     if constexpr (!KLDS) kreg[kc] = kv;
     vreg[kc] = vv;
   }
+  // Fixed-point scale of the dQ accumulator for this head (see the file
+  // comment), from the preprocess maxima: x -> rint((x / B) * 2^30), with
+  // 1 / B taken once.  Workgroup 0 of the head records B for the conversion.
+  float dq_inv_bound;
+  {
+    __shared__ float red[NW][3];
+    const float* part = p.bound_part + static_cast<int64_t>(bh) * 3 * p.npart;
+    float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f;
+    for (int c = tid; c < p.npart; c += THREADS) {
+      m0 = fmaxf(m0, part[c]);
+      m1 = fmaxf(m1, part[p.npart + c]);
+      m2 = fmaxf(m2, part[2 * p.npart + c]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
+      m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+      m2 = fmaxf(m2, __shfl_xor(m2, off, 64));
+    }
+    if (lane == 0) {
+      red[wave][0] = m0;
+      red[wave][1] = m1;
+      red[wave][2] = m2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      m0 = fmaxf(m0, red[w][0]);
+      m1 = fmaxf(m1, red[w][1]);
+      m2 = fmaxf(m2, red[w][2]);
+    }
+    // A bound that is not a finite normal float (every gradient below
+    // 1.2e-38, or non-finite inputs) gives dQ = 0.
+    const float bound = (4.0f * D) * m0 * m1 * m2;
+    const bool usable = bound >= 1.2e-38f && bound < INFINITY;
+    dq_inv_bound = usable ? 1.0f / bound : 0.0f;
+    if (kblk == 0 && tid == 0) p.dq_bound[bh] = usable ? bound : 0.0f;
+  }
+
   // The workgroup's K rows in LDS (B operand of dQ = dS K).
   for (int c = tid; c < BKV * CPR; c += THREADS) {
     const int row = c / CPR;
@@ -229,9 +320,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     dvacc[db] = (f32x16){};
   }
 
-  // ---- dQ: one 32x32 block per wave per tile, added with fp32 atomics.
+  // ---- dQ: one 32x32 block per wave per tile, added with integer atomics
+  // in units of B / 2^30 (rounded to nearest).
   // C value i of block (qb, db): query qt + 32*qb + c_row(i, hh), d = 32*db + l32.
   f32x16 dqacc[BPW];
+  auto to_fix = [&](float x) {
+    return static_cast<int32_t>(__builtin_rintf((x * dq_inv_bound) * 1073741824.0f));
+  };
   auto dq_atomics = [&](int qt) {
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
@@ -239,16 +334,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       if (blk < NBLK) {
         const int qb = blk / DB, db = blk % DB;
         const int qr = qt + 32 * qb + 4 * hh;
-        float* base = dq_acc + static_cast<int64_t>(qr) * D + 32 * db + l32;
+        int32_t* base = dq_acc + static_cast<int64_t>(qr) * D + 32 * db + l32;
         if (qt + 32 * qb + 31 < N) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, dqacc[bi][i]);
+            atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, to_fix(dqacc[bi][i]));
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (qr + 8 * (i / 4) + (i % 4) < N)
-              atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, dqacc[bi][i]);
+              atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, to_fix(dqacc[bi][i]));
         }
       }
     }
@@ -410,22 +505,28 @@ struct BwdShape {
 };
 
 // ------------------------------------------------------------------ kernel 3
+// Grid (ceil(N / RPB), B*H): dq = scale * B * (accumulator / 2^30).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
   constexpr int TPR = D / 8;
   constexpr int RPB = 256 / TPR;
   const int tid = threadIdx.x;
   const int part = tid % TPR;
-  const int64_t total = static_cast<int64_t>(p.B) * p.H * p.N;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + tid / TPR;
-  if (row >= total) return;
-  const int n = static_cast<int>(row % p.N);
-  const int bh = static_cast<int>(row / p.N);
+  const int bh = blockIdx.y;
+  const int n = static_cast<int>(blockIdx.x) * RPB + tid / TPR;
+  if (n >= p.N) return;
   const int b = bh / p.H, h = bh % p.H;
-  const float* a = p.dq_accum + row * D + part * 8;
+  const int32_t* a = p.dq_fix + (static_cast<int64_t>(bh) * p.N + n) * D + part * 8;
+  const u32x4 a0 = ldg16(a);
+  const u32x4 a1 = ldg16(a + 4);
+  const float unit = p.dq_bound[bh] * p.scale;
+  constexpr float kInv30 = 1.0f / 1073741824.0f;
   float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = a[e] * p.scale;
+  for (int e = 0; e < 4; ++e) {
+    v[e] = (static_cast<float>(static_cast<int32_t>(a0[e])) * kInv30) * unit;
+    v[e + 4] = (static_cast<float>(static_cast<int32_t>(a1[e])) * kInv30) * unit;
+  }
   stg16(p.dq + b * p.sdq.b + static_cast<int64_t>(n) * p.sdq.n + h * p.sdq.h + part * 8, pack8<T>(v));
 }
 
@@ -435,12 +536,12 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   constexpr int NW = Sh::NW;
   BwdParams p = p_in;
   p.num_kblocks = (p.N + BwdCfg<D, NW, Sh::BQ>::BKV - 1) / BwdCfg<D, NW, Sh::BQ>::BKV;
-  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
   constexpr int RPB = 256 / (D / 8);
-  const unsigned row_blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
+  p.npart = (p.N + RPB - 1) / RPB;
+  const dim3 row_grid(static_cast<unsigned>(p.npart), static_cast<unsigned>(p.B * p.H));
   hipError_t e = hipSuccess;
   if (stages & 1u) {
-    hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3(row_blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), row_grid, dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2u) {
@@ -450,7 +551,7 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 4u) {
-    hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), dim3(row_blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, s, p);
     e = hipGetLastError();
   }
   return e;

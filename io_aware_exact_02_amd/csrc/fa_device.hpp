@@ -107,6 +107,18 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b) {
   return s;
 }
 
+// Largest magnitude among eight packed halves.
+template <typename T>
+__device__ __forceinline__ float absmax8(const u32x4& a) {
+  float m = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    m = fmaxf(m, fabsf(half_bits_to_float<T>(a[w] & 0xffffu)));
+    m = fmaxf(m, fabsf(half_bits_to_float<T>(a[w] >> 16)));
+  }
+  return m;
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

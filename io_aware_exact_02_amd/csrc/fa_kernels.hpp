@@ -33,11 +33,14 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dvec;      // workspace: [B, H, N]
-  float* dq_accum;  // workspace: [B, H, N, D]
+  float* dvec;        // workspace: [B, H, N]
+  int32_t* dq_fix;    // workspace: [B, H, N, D] dQ accumulator, fixed point
+  float* bound_part;  // workspace: [B*H, 3, npart] maxima per row block
+  float* dq_bound;    // workspace: [B*H] dQ bound B; one fixed-point unit = B / 2^30
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, N;
   int num_kblocks;  // ceil(N / keys per workgroup)
+  int npart;        // row blocks per head in bound_part
   float scale;
   float c;  // scale * log2(e)
 };

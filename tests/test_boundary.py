@@ -49,9 +49,15 @@ def test_workspace_bytes_is_linear_in_n():
     def a256(x):
         return (x + 255) // 256 * 256
 
-    for (B, H, N, D) in [(1, 1, 1, 64), (2, 12, 2048, 64), (1, 16, 16384, 64), (1, 8, 8192, 128)]:
-        rows = B * H * N
-        assert lib.fa_bwd_workspace_bytes(B, H, N, D) == a256(4 * rows) + a256(4 * rows * D)
+    # Dvec, the int32 dQ accumulator, three maxima per 16-row block and one
+    # fixed-point unit per head: O(N*D) per head, no N*N term.
+    for (B, H, N, D) in [(1, 1, 1, 64), (2, 12, 2048, 64), (1, 16, 16384, 64), (1, 8, 8192, 128),
+                         (3, 5, 1000, 128)]:
+        heads, rows = B * H, B * H * N
+        want = (a256(4 * rows) + a256(4 * rows * D) + a256(4 * 3 * heads * ((N + 15) // 16))
+                + a256(4 * heads))
+        assert lib.fa_bwd_workspace_bytes(B, H, N, D) == want
+        assert lib.fa_bwd_workspace_bytes(B, H, 2 * N, D) < 2 * want + 4 * 256
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64) == 0
 
 
