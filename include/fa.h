@@ -53,8 +53,10 @@ typedef enum {
                              causal not 0/1, unknown dtype, workspace too small */
   FA_ERR_UNSUPPORTED = 2, /* D not 64/128, tensor pointer not 16-byte aligned
                              (lse: 4-byte; workspace: 256-byte),
-                             b/n/h stride not a multiple of 8 elements, or a
-                             size whose element offsets overflow int64 */
+                             b/n/h stride not a multiple of 8 elements, a
+                             size whose element offsets overflow int64, more
+                             than 2^31 rows B*H*N, or (fa_bwd) N*D*4 bytes
+                             per head at or above 2^31 */
   FA_ERR_HIP = 3          /* a HIP runtime call failed (no device, launch error) */
 } fa_status;
 

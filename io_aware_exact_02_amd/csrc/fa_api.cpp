@@ -122,6 +122,8 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
     return FA_ERR_INVALID_ARG;
   int st = check_sizes(B, H, N, D, causal, scale, dtype);
   if (st != FA_OK) return st;
+  // One head's dQ accumulator is addressed as a buffer of N*D*4 bytes.
+  if (static_cast<int64_t>(N) * D * 4 > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
   if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, D)) return FA_ERR_INVALID_ARG;
   for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq),
                           static_cast<const void*>(dk), static_cast<const void*>(dv)}) {

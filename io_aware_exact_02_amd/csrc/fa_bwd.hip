@@ -32,7 +32,7 @@
 // huge inputs would under- or overflow.  Every partial sum is rounded to the nearest unit; the
 // total stays within 2^30 units, so the 32-bit sum is exact whatever the
 // order of the adds -- dQ is deterministic -- and its error is at most half
-// a unit per key block.
+// a unit per key block (rounding half up, v_cvt_rpi_i32_f32).
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -167,6 +167,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const float* lse_row = p.lse + static_cast<int64_t>(bh) * N;
   const float* dvec_row = p.dvec + static_cast<int64_t>(bh) * N;
   int32_t* dq_acc = p.dq_fix + static_cast<int64_t>(bh) * N * D;
+  // The head's accumulator as a buffer: row offsets go in the scalar offset.
+  const __amdgpu_buffer_rsrc_t dq_rs = raw_rsrc(dq_acc, N * D * 4);
 
   const int kb0 = kblk * BKV;
   const int kw0 = kb0 + 32 * wave;
@@ -187,9 +189,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     vreg[kc] = vv;
   }
   // Fixed-point scale of the dQ accumulator for this head (see the file
-  // comment), from the preprocess maxima: x -> rint((x / B) * 2^30), with
-  // 1 / B taken once.  Workgroup 0 of the head records B for the conversion.
-  float dq_inv_bound;
+  // comment), from the preprocess maxima: x -> round(x * 2^30 / B).  B is
+  // raised to at least 2^-96 so that the scale stays finite; a larger B is
+  // still a bound, and gradients that small keep an absolute resolution of
+  // 2^-126.  Workgroup 0 of the head records B for the conversion.
+  float dq_scale;
   {
     __shared__ float red[NW][3];
     const float* part = p.bound_part + static_cast<int64_t>(bh) * 3 * p.npart;
@@ -217,11 +221,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       m1 = fmaxf(m1, red[w][1]);
       m2 = fmaxf(m2, red[w][2]);
     }
-    // A bound that is not a finite normal float (every gradient below
-    // 1.2e-38, or non-finite inputs) gives dQ = 0.
-    const float bound = (4.0f * D) * m0 * m1 * m2;
-    const bool usable = bound >= 1.2e-38f && bound < INFINITY;
-    dq_inv_bound = usable ? 1.0f / bound : 0.0f;
+    // A non-finite bound (non-finite inputs) gives dQ = 0.
+    const float bound = fmaxf((4.0f * D) * m0 * m1 * m2, 0x1p-96f);
+    const bool usable = bound < INFINITY;
+    dq_scale = usable ? 0x1p30f / bound : 0.0f;
     if (kblk == 0 && tid == 0) p.dq_bound[bh] = usable ? bound : 0.0f;
   }
 
@@ -324,9 +327,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // in units of B / 2^30 (rounded to nearest).
   // C value i of block (qb, db): query qt + 32*qb + c_row(i, hh), d = 32*db + l32.
   f32x16 dqacc[BPW];
-  auto to_fix = [&](float x) {
-    return static_cast<int32_t>(__builtin_rintf((x * dq_inv_bound) * 1073741824.0f));
-  };
   auto dq_atomics = [&](int qt) {
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
@@ -334,16 +334,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       if (blk < NBLK) {
         const int qb = blk / DB, db = blk % DB;
         const int qr = qt + 32 * qb + 4 * hh;
-        int32_t* base = dq_acc + static_cast<int64_t>(qr) * D + 32 * db + l32;
+        const int voff = (qr * D + 32 * db + l32) * 4;  // bytes, this lane
+        auto add = [&](int i) {
+          __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(cvt_rpi(dqacc[bi][i] * dq_scale), dq_rs,
+                                                         voff, (8 * (i / 4) + (i % 4)) * D * 4, 0);
+        };
         if (qt + 32 * qb + 31 < N) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, to_fix(dqacc[bi][i]));
+          for (int i = 0; i < 16; ++i) add(i);
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (qr + 8 * (i / 4) + (i % 4) < N)
-              atomicAdd(base + (8 * (i / 4) + (i % 4)) * D, to_fix(dqacc[bi][i]));
+            if (qr + 8 * (i / 4) + (i % 4) < N) add(i);
         }
       }
     }
@@ -403,6 +405,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       pS[qb][0] = pack8<T>(dsv);
       pS[qb][1] = pack8<T>(dsv + 8);
     }
+    // LLVM's MFMA interleaving strategy 1 for the rest of the tile: measured
+    // 4-7% faster at head_dim 64, slower at 128.
+    if constexpr (D == 64) __builtin_amdgcn_iglp_opt(1);
     // dV += P^T dO, dK += dS^T Q over the tile's query rows.
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {

@@ -107,6 +107,21 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b) {
   return s;
 }
 
+// Raw buffer resource (stride 0) over `bytes` bytes at p, for buffer
+// instructions: a uniform 64-bit base in scalar registers plus 32-bit vector
+// and scalar offsets, so per-access address arithmetic stays 32-bit.  The
+// last dword is the gfx9 raw-buffer format word (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0), bytes, 0x00020000);
+}
+
+// fp32 -> int32 rounding half up in one instruction: floor(x + 0.5).
+__device__ __forceinline__ int32_t cvt_rpi(float x) {
+  int32_t r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // Largest magnitude among eight packed halves.
 template <typename T>
 __device__ __forceinline__ float absmax8(const u32x4& a) {
