@@ -22,7 +22,10 @@ Prints ONE JSON line.  Besides the headline value it carries
   cpu_baseline : the fp64 CPU oracle timed on a bounded sample (c5 heads);
   per_config   : forward / backward times and TFLOP/s per workload;
   memory_c3    : peak device memory of fused fwd+bwd vs an unfused S/P
-                 PyTorch baseline at c3 (untimed pass).
+                 PyTorch baseline at c3 (untimed pass);
+  pages_sweep  : the pages' own forward speed comparison (standard fp16
+                 attention vs the fused kernel, B=2 H=8 D=64 fp16 at
+                 N = 2048/4096/8192, causal at 4096), untimed by the step.
 """
 
 from __future__ import annotations
@@ -153,6 +156,66 @@ def unfused_memory_c3(torch, fa, w, inp):
     return res
 
 
+def pages_sweep(torch, fa):
+    """The speed comparison of the hotelren.com FlashAttention-2 walkthrough,
+    section 4, on this GPU: forward time of the standard three-step attention
+    (S = QK^T / sqrt(d), softmax, O = PV, all in fp16 with S and P
+    materialised) against the fused kernel, the speedup, and the largest
+    difference between the two outputs, for B=2, H=8, D=64 fp16 at N = 2048,
+    4096, 8192; then the causal forward at N = 4096 against the non-causal
+    one.  Also reported: each output's largest error against an fp32
+    reference computed on the device."""
+    from workloads import PAGES_SWEEP, make_inputs
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, iters=10, warm=3):
+        for _ in range(warm):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    def standard(qt, kt, vt, causal, D, acc_dtype):
+        # contiguous operands only; the mask is applied before the softmax
+        attn = torch.matmul(qt.to(acc_dtype), kt.transpose(-2, -1).contiguous().to(acc_dtype))
+        attn = attn / (D ** 0.5)
+        if causal:
+            n = attn.shape[-1]
+            mask = torch.ones(n, n, dtype=torch.bool, device=dev).triu(1)
+            attn = attn.masked_fill(mask, float("-inf"))
+        attn = torch.softmax(attn, dim=-1)
+        return torch.matmul(attn, vt.to(acc_dtype))
+
+    rows = []
+    fused_ms = {}
+    for name, w in PAGES_SWEEP.items():
+        inp = make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        qt, kt, vt = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+        t_std = timed(lambda: standard(qt, kt, vt, w.causal, w.D, q.dtype))
+        t_fa = timed(lambda: fa.fwd(q, k, v, causal=w.causal))
+        o_std = standard(qt, kt, vt, w.causal, w.D, q.dtype).transpose(1, 2).float()
+        o_fa = fa.fwd(q, k, v, causal=w.causal)[0].float()
+        o_ref = standard(qt, kt, vt, w.causal, w.D, torch.float32).transpose(1, 2)
+        fused_ms[name] = t_fa
+        rows.append({"seq_len": w.N, "causal": w.causal, "shape": w.describe(),
+                     "standard_ms": round(t_std, 4), "fused_ms": round(t_fa, 4),
+                     "speedup": round(t_std / t_fa, 2),
+                     "max_err": float((o_std - o_fa).abs().max()),
+                     "max_err_fp32_ref": {"standard": float((o_std - o_ref).abs().max()),
+                                          "fused": float((o_fa - o_ref).abs().max())}})
+        del q, k, v, qt, kt, vt, o_std, o_fa, o_ref
+        torch.cuda.empty_cache()
+    return {"rows": rows,
+            "causal_vs_noncausal_fused_speedup_N4096": round(fused_ms["s4096"] / fused_ms["s4096c"], 2)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +225,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU oracle baseline (0 = skip)")
     ap.add_argument("--no-memory", action="store_true", help="skip the c3 memory comparison")
+    ap.add_argument("--no-pages-sweep", action="store_true",
+                    help="skip the standard-vs-fused forward sweep of the pages (N=2048..8192)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise kernel that reads and "
                          "writes this many MiB (calibrates HBM byte counters)")
@@ -284,6 +349,10 @@ def main(argv=None):
         c3 = next(c for c in cases if c["w"].name == "c3")
         memory = unfused_memory_c3(torch, fa, c3["w"], c3["inp"])
 
+    sweep = None
+    if not args.no_pages_sweep:
+        sweep = pages_sweep(torch, fa)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -311,6 +380,7 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "per_config": per_config,
         "memory_c3": memory,
+        "pages_sweep": sweep,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -77,7 +77,8 @@ def run(cmd, timeout, log):
 
 def bench_cmd(workloads, steps, calib_mib):
     return [sys.executable, BENCH, "--steps", str(steps), "--warmup", "2", "--cpu-seconds", "0",
-            "--no-memory", "--workloads", workloads, "--copy-calibration-mib", str(calib_mib)]
+            "--no-memory", "--no-pages-sweep", "--workloads", workloads,
+            "--copy-calibration-mib", str(calib_mib)]
 
 
 def rocprof(args, out, bench):
@@ -158,7 +159,8 @@ def main(argv=None):
              "command: python -m io_aware_exact_02_amd.rocprof_harness --raw <dir> "
              f"--workloads {a.workloads} --steps {a.steps} --calib-mib {a.calib_mib}",
              "  runs: rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py "
-             f"--steps {a.steps} --warmup 2 --cpu-seconds 0 --no-memory --workloads {a.workloads} "
+             f"--steps {a.steps} --warmup 2 --cpu-seconds 0 --no-memory --no-pages-sweep "
+             f"--workloads {a.workloads} "
              f"--copy-calibration-mib {a.calib_mib}",
              "        and the same command under rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
              "SQ_INSTS_VALU_MFMA_MOPS_F16 / --pmc FETCH_SIZE / --pmc WRITE_SIZE",

@@ -14,7 +14,7 @@ import torch
 
 import io_aware_exact_02_amd as fa
 from oracle import attention as oa
-from workloads import WORKLOADS, make_inputs, random_qkv, sample_rows
+from workloads import PAGES_SWEEP, WORKLOADS, make_inputs, random_qkv, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +189,31 @@ def test_config_c5_sampled():
     for (b, h) in heads:
         assert_grad("dK", got["dK"][b, :, h], dK[b, :, h], f"c5 head {h}")
         assert_grad("dV", got["dV"][b, :, h], dV[b, :, h], f"c5 head {h}")
+
+
+@pytest.mark.parametrize("name", ["s2048", "s4096", "s8192", "s4096c"])
+def test_pages_sweep_shapes(name):
+    """The pages' speed-sweep shapes (B=2 H=8 D=64 fp16 [B,N,H,D]): O, LSE
+    and dQ at 128 sampled rows of every head (row-local, exact), dK and dV in
+    full on the first and last head."""
+    w = PAGES_SWEEP[name]
+    _say("case", w.describe())
+    inp = make_inputs(w)
+    got = gpu_forward_backward(inp, w.causal)
+    rows = sample_rows(w.N, 128, seed=w.seed)
+    for b in range(w.B):
+        for h in range(w.H):
+            r = oa.attention_rows(inp["q"], inp["k"], inp["v"], inp["do"], b, h, rows,
+                                  causal=w.causal)
+            sub = {"O": got["O"][b, rows, h], "LSE": got["LSE"][b, h, rows]}
+            assert_forward(sub, r["O"], r["LSE"], f"{name} b{b} h{h}")
+            assert_grad("dQ", got["dQ"][b, rows, h], r["dQ"], f"{name} b{b} h{h}")
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    _, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=w.causal,
+                                      heads=heads)
+    for (b, h) in heads:
+        assert_grad("dK", got["dK"][b, :, h], dK[b, :, h], f"{name} b{b} h{h}")
+        assert_grad("dV", got["dV"][b, :, h], dV[b, :, h], f"{name} b{b} h{h}")
 
 
 # ------------------------------------------------------------ properties

@@ -62,6 +62,17 @@ WORKLOADS = {
 }
 
 
+# The speed sweep of the hotelren.com FlashAttention-2 walkthrough, section
+# 4: B=2, H=8, D=64, fp16 q, k, v in [B, N, H, D] at N = 2048, 4096 and 8192
+# (non-causal), plus the causal run at N = 4096.
+PAGES_SWEEP = {
+    "s2048": Workload("s2048", 2, 8, 2048, 64, "f16", False, "bnhd", 1102),
+    "s4096": Workload("s4096", 2, 8, 4096, 64, "f16", False, "bnhd", 1104),
+    "s8192": Workload("s8192", 2, 8, 8192, 64, "f16", False, "bnhd", 1108),
+    "s4096c": Workload("s4096c", 2, 8, 4096, 64, "f16", True, "bnhd", 1114),
+}
+
+
 def _randn(shape, gen: torch.Generator, dtype: torch.dtype) -> torch.Tensor:
     return torch.randn(shape, dtype=torch.float32, generator=gen).to(dtype)
 
