@@ -16,7 +16,15 @@ What it computes, and where the pages define it:
   walkthrough, section 5).
 * The causal variant masks the upper triangle (keys j > query i): the
   "causal (lower-triangular) mask" limit on the bjdmk.com.cn page, section
-  "实战集成".
+  "实战集成".  With N_q queries against N_k keys the triangle is aligned to
+  the last query and key (query i sees keys j <= i + N_k - N_q), which is the
+  same mask when N_q = N_k and makes N_q new queries against an N_k-key
+  history the last N_q rows of the square problem.  A query that sees no key
+  gets O = 0 and LSE = -inf (the logsumexp of an empty set).
+* Partial results over disjoint key sets combine exactly through the LSE:
+  ``LSE = ln sum_r exp(LSE_r)``, ``O = sum_r exp(LSE_r - LSE) O_r`` -- the
+  logsumexp statistic the walkthrough keeps (section 3.1) is what makes
+  such a merge possible.
 * ``LSE_i = m_i + ln(l_i)``, the per-row logsumexp of the scaled scores, which
   is the one statistic FlashAttention-2 keeps for the backward pass
   (hotelren.com walkthrough, section 3.1).
@@ -53,23 +61,29 @@ def default_scale(D: int) -> float:
     return 1.0 / np.sqrt(D)
 
 
-def _head_rows(Q, K, V, rows, causal, scale, dO=None):
+def _head_rows(Q, K, V, rows, causal, scale, dO=None, offset=0):
     """Softmax attention for the query rows ``rows`` of one (batch, head).
 
-    Q: [R, D] (the query vectors of ``rows``), K, V: [N, D], dO: [R, D].
+    Q: [R, D] (the query vectors of ``rows``), K, V: [Nk, D], dO: [R, D].
+    ``offset`` = N_k - N_q: with ``causal`` query i sees keys j <= i + offset.
     Returns a dict with S, P, O, LSE and, when dO is given, dP, Dvec, dS,
-    dQ (rows only) and the contributions of these rows to dK, dV.
+    dQ (rows only) and the contributions of these rows to dK, dV.  Rows that
+    see no key have P = 0, O = 0, LSE = -inf and zero gradients.
     """
-    N = K.shape[0]
-    S = scale * (Q @ K.T)                                  # [R, N]
+    Nk = K.shape[0]
+    S = scale * (Q @ K.T)                                  # [R, Nk]
     if causal:
-        cols = np.arange(N)[None, :]
-        S = np.where(cols > np.asarray(rows)[:, None], -np.inf, S)
-    m = S.max(axis=1)                                      # running max is not
-    E = np.exp(S - m[:, None])                             # needed: whole row
+        cols = np.arange(Nk)[None, :]
+        S = np.where(cols > np.asarray(rows)[:, None] + offset, -np.inf, S)
+    m = S.max(axis=1) if Nk else np.full(S.shape[0], -np.inf)
+    empty = np.isneginf(m)                                 # no visible key
+    m_safe = np.where(empty, 0.0, m)                       # running max is not
+    E = np.exp(S - m_safe[:, None])                        # needed: whole row
     l = E.sum(axis=1)
-    P = E / l[:, None]
-    out = {"S": S, "P": P, "O": P @ V, "LSE": m + np.log(l)}
+    P = E / np.where(empty, 1.0, l)[:, None]
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    out = {"S": S, "P": P, "O": P @ V, "LSE": lse}
     if dO is not None:
         dP = dO @ V.T
         dvec_p = (P * dP).sum(axis=1)                      # rowsum(P o dP)
@@ -89,9 +103,11 @@ def _head_rows(Q, K, V, rows, causal, scale, dO=None):
 
 def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
                       row_chunk: int = DEFAULT_ROW_CHUNK):
-    """O [B,N,H,D] and LSE [B,H,N] (natural log) for q, k, v in [B,N,H,D]."""
+    """O [B,Nq,H,D] and LSE [B,H,Nq] (natural log) for q [B,Nq,H,D] and
+    k, v [B,Nk,H,D]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, H, D = q.shape
+    offset = k.shape[1] - N
     scale = default_scale(D) if scale is None else float(scale)
     O = np.zeros((B, N, H, D))
     LSE = np.zeros((B, H, N))
@@ -100,22 +116,44 @@ def attention_forward(q, k, v, causal: bool = False, scale: float | None = None,
             K, V = k[b, :, h, :], v[b, :, h, :]
             for r0 in range(0, N, row_chunk):
                 rows = np.arange(r0, min(N, r0 + row_chunk))
-                res = _head_rows(q[b, rows, h, :], K, V, rows, causal, scale)
+                res = _head_rows(q[b, rows, h, :], K, V, rows, causal, scale, offset=offset)
                 O[b, rows, h, :] = res["O"]
                 LSE[b, h, rows] = res["LSE"]
+    return O, LSE
+
+
+def merge_partials(O_parts, LSE_parts):
+    """Exact combination of attention results over disjoint key sets.
+
+    O_parts: [P, B, N, H, D], LSE_parts: [P, B, H, N] (natural log; -inf for
+    a part in which a row sees no key).  Returns O [B,N,H,D], LSE [B,H,N]:
+    LSE = ln sum_r exp(LSE_r) and O = sum_r exp(LSE_r - LSE) O_r, with O = 0
+    and LSE = -inf for rows no part covers.
+    """
+    O_parts, LSE_parts = _f64(O_parts), _f64(LSE_parts)
+    m = LSE_parts.max(axis=0)                              # [B, H, N]
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(LSE_parts - m_safe[None])                   # [P, B, H, N]
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        LSE = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))
+    wn = w / np.where(empty, 1.0, tot)[None]               # weights exp(LSE_r - LSE)
+    O = np.einsum("pbhn,pbnhd->bnhd", wn, O_parts)
     return O, LSE
 
 
 def attention_backward(q, k, v, dout, causal: bool = False,
                        scale: float | None = None,
                        row_chunk: int = DEFAULT_ROW_CHUNK, heads=None):
-    """dQ, dK, dV (each [B,N,H,D], fp64) of  L = sum(O o dout).
+    """dQ [B,Nq,H,D], dK, dV [B,Nk,H,D] (fp64) of  L = sum(O o dout).
 
     ``heads``: optional list of (b, h) pairs to evaluate; the others are left
     zero (used where a full-size check covers only some heads).
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, N, H, D = q.shape
+    offset = k.shape[1] - N
     scale = default_scale(D) if scale is None else float(scale)
     dQ = np.zeros_like(q)
     dK = np.zeros_like(k)
@@ -126,7 +164,7 @@ def attention_backward(q, k, v, dout, causal: bool = False,
         for r0 in range(0, N, row_chunk):
             rows = np.arange(r0, min(N, r0 + row_chunk))
             res = _head_rows(q[b, rows, h, :], K, V, rows, causal, scale,
-                             dO=dout[b, rows, h, :])
+                             dO=dout[b, rows, h, :], offset=offset)
             dQ[b, rows, h, :] = res["dQ"]
             dK[b, :, h, :] += res["dK_part"]
             dV[b, :, h, :] += res["dV_part"]
@@ -146,22 +184,23 @@ def attention_rows(q, k, v, dout, b: int, h: int, rows, causal: bool = False,
     rows = np.asarray(rows)
     dO = None if dout is None else _f64(dout)[b, rows, h, :]
     res = _head_rows(q[b, rows, h, :], k[b, :, h, :], v[b, :, h, :], rows,
-                     causal, scale, dO=dO)
+                     causal, scale, dO=dO, offset=k.shape[1] - q.shape[1])
     keep = ("O", "LSE") if dO is None else ("O", "LSE", "Dvec", "dQ")
     return {key: res[key] for key in keep}
 
 
 def attention_probs(q, k, causal: bool = False, scale: float | None = None):
-    """The full probability matrix P [B,H,N,N] (small inputs only)."""
+    """The full probability matrix P [B,H,Nq,Nk] (small inputs only)."""
     q, k = _f64(q), _f64(k)
     B, N, H, D = q.shape
+    Nk = k.shape[1]
     scale = default_scale(D) if scale is None else float(scale)
-    P = np.zeros((B, H, N, N))
-    zeros = np.zeros((N, D))
+    P = np.zeros((B, H, N, Nk))
+    zeros = np.zeros((Nk, D))
     for b in range(B):
         for h in range(H):
             P[b, h] = _head_rows(q[b, :, h, :], k[b, :, h, :], zeros,
-                                 np.arange(N), causal, scale)["P"]
+                                 np.arange(N), causal, scale, offset=Nk - N)["P"]
     return P
 
 

@@ -251,10 +251,100 @@ def pin_sampled_rows_match_full():
         assert np.max(np.abs(g2[0] - dQ)) <= 1e-14
 
 
+def _close(a, b, tol=1e-12):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin) and np.array_equal(a[~fin], b[~fin])
+    assert np.max(np.abs(a[fin] - b[fin]), initial=0.0) <= tol * max(1.0, np.max(np.abs(b[fin]), initial=0.0))
+
+
+def pin_offset_causal_matches_square():
+    """P12: N_q < N_k queries under the causal mask aligned to the last key
+    see exactly what the last N_q rows of the square causal problem see:
+    square problem = queries [prefix; q] against the same keys, with dO = 0
+    on the prefix rows (so they add nothing to dK, dV).  The last query
+    sees every key, as without the mask."""
+    B, Nq, Nk, H, D = 2, 5, 12, 2, 4
+    q, do = _rand((B, Nq, H, D), 121), _rand((B, Nq, H, D), 124)
+    k, v = _rand((B, Nk, H, D), 122), _rand((B, Nk, H, D), 123)
+    prefix = _rand((B, Nk - Nq, H, D), 125)
+    qs = np.concatenate([prefix, q], axis=1)
+    dos = np.concatenate([np.zeros_like(prefix), do], axis=1)
+    for scale in (None, 0.6):
+        O, LSE = oa.attention_forward(q, k, v, causal=True, scale=scale)
+        Os, LSEs = oa.attention_forward(qs, k, v, causal=True, scale=scale)
+        _close(O, Os[:, Nk - Nq:])
+        _close(LSE, LSEs[:, :, Nk - Nq:])
+        dQ, dK, dV = oa.attention_backward(q, k, v, do, causal=True, scale=scale)
+        dQs, dKs, dVs = oa.attention_backward(qs, k, v, dos, causal=True, scale=scale)
+        _close(dQ, dQs[:, Nk - Nq:])
+        _close(dK, dKs)
+        _close(dV, dVs)
+        On, LSEn = oa.attention_forward(q, k, v, causal=False, scale=scale)
+        _close(O[:, -1], On[:, -1])
+        _close(LSE[:, :, -1], LSEn[:, :, -1])
+
+
+def pin_offset_more_queries_than_keys():
+    """P13: with N_q > N_k and the same alignment, the first N_q - N_k
+    queries see no key (O = 0, LSE = -inf, dQ = 0) and the rest are the
+    square causal problem on the last N_k queries."""
+    B, Nq, Nk, H, D = 1, 9, 4, 2, 3
+    q, do = _rand((B, Nq, H, D), 131), _rand((B, Nq, H, D), 134)
+    k, v = _rand((B, Nk, H, D), 132), _rand((B, Nk, H, D), 133)
+    O, LSE = oa.attention_forward(q, k, v, causal=True)
+    dQ, dK, dV = oa.attention_backward(q, k, v, do, causal=True)
+    cut = Nq - Nk
+    assert np.all(O[:, :cut] == 0.0) and np.all(np.isneginf(LSE[:, :, :cut]))
+    assert np.all(dQ[:, :cut] == 0.0)
+    Os, LSEs = oa.attention_forward(q[:, cut:], k, v, causal=True)
+    dQs, dKs, dVs = oa.attention_backward(q[:, cut:], k, v, do[:, cut:], causal=True)
+    _close(O[:, cut:], Os)
+    _close(LSE[:, :, cut:], LSEs)
+    _close(dQ[:, cut:], dQs)
+    _close(dK, dKs)
+    _close(dV, dVs)
+
+
+def pin_merge_partials():
+    """P14: attention over a key set split into chunks, merged through the
+    LSE, equals attention over the whole set: non-causal with three chunks;
+    causal (N_k > N_q) as a non-causal part over the keys every query sees
+    plus the causal part over the rest; a part in which no row sees a key
+    changes nothing.  The merged LSE matches scipy's logsumexp of the parts."""
+    B, Nq, Nk, H, D = 2, 6, 11, 2, 5
+    q = _rand((B, Nq, H, D), 141)
+    k, v = _rand((B, Nk, H, D), 142), _rand((B, Nk, H, D), 143)
+    O, LSE = oa.attention_forward(q, k, v)
+    cuts = [0, 4, 8, Nk]
+    parts = [oa.attention_forward(q, k[:, a:b], v[:, a:b]) for a, b in zip(cuts, cuts[1:])]
+    Op = np.stack([p[0] for p in parts])
+    Lp = np.stack([p[1] for p in parts])
+    Om, Lm = oa.merge_partials(Op, Lp)
+    _close(Om, O)
+    _close(Lm, LSE)
+    _close(Lm, scipy.special.logsumexp(Lp, axis=0))
+    # a part that covers no key for any row
+    Om2, Lm2 = oa.merge_partials(np.concatenate([Op, np.zeros_like(Op[:1])]),
+                                 np.concatenate([Lp, np.full_like(Lp[:1], -np.inf)]))
+    _close(Om2, O)
+    _close(Lm2, LSE)
+    # causal, N_k > N_q: keys [0, s) with s <= N_k - N_q + 1 are seen by every query
+    s = Nk - Nq + 1
+    Oc, LSEc = oa.attention_forward(q, k, v, causal=True)
+    p0 = oa.attention_forward(q, k[:, :s], v[:, :s], causal=False)
+    p1 = oa.attention_forward(q, k[:, s:], v[:, s:], causal=True)
+    Omc, Lmc = oa.merge_partials(np.stack([p0[0], p1[0]]), np.stack([p0[1], p1[1]]))
+    _close(Omc, Oc)
+    _close(Lmc, LSEc)
+
+
 ALL_PINS = [pin_rows_sum_to_one, pin_constant_key, pin_causal_rows, pin_closed_forms,
             pin_gradient_sums, pin_permutations, pin_dvec_identity,
             pin_finite_differences, pin_library_routines, pin_worked_example,
-            pin_sampled_rows_match_full]
+            pin_sampled_rows_match_full, pin_offset_causal_matches_square,
+            pin_offset_more_queries_than_keys, pin_merge_partials]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -276,10 +366,15 @@ MUTANTS = {
     "dropped_scale_in_S": ("S = scale * (Q @ K.T)", "S = (Q @ K.T)"),
     "mask_includes_diagonal": ("cols > np.asarray(rows)", "cols >= np.asarray(rows)"),
     "mask_wrong_triangle": ("cols > np.asarray(rows)", "cols < np.asarray(rows)"),
-    "lse_without_max": ('"LSE": m + np.log(l)', '"LSE": np.log(l)'),
-    "lse_log2": ('"LSE": m + np.log(l)', '"LSE": m + np.log2(l)'),
-    "no_max_shift_in_lse": ("E = np.exp(S - m[:, None])", "E = np.exp(S)"),
-    "normaliser_transposed": ("P = E / l[:, None]", "P = E / l[None, :]"),
+    "lse_without_max": ("m_safe + np.log(np.where(empty, 1.0, l))",
+                        "np.log(np.where(empty, 1.0, l))"),
+    "lse_log2": ("m_safe + np.log(np.where(empty, 1.0, l))",
+                 "m_safe + np.log2(np.where(empty, 1.0, l))"),
+    "no_max_shift_in_lse": ("E = np.exp(S - m_safe[:, None])", "E = np.exp(S)"),
+    "normaliser_transposed": ("P = E / np.where(empty, 1.0, l)[:, None]",
+                              "P = E / np.where(empty, 1.0, l)[None, :]"),
+    "offset_ignored": ("[:, None] + offset, -np.inf", "[:, None], -np.inf"),
+    "offset_sign": ("[:, None] + offset, -np.inf", "[:, None] - offset, -np.inf"),
     "output_transposed": ('"O": P @ V', '"O": P.T @ V'),
     "dP_uses_K": ("dP = dO @ V.T", "dP = dO @ K.T"),
     "dS_sign": ("dS = P * (dP - dvec_p[:, None])", "dS = P * (dvec_p[:, None] - dP)"),
@@ -296,6 +391,7 @@ MUTANTS = {
 # slow; two small shapes cover every term).
 QUICK_PINS = [pin_worked_example, pin_rows_sum_to_one, pin_constant_key,
               pin_causal_rows, pin_gradient_sums, pin_library_routines,
+              pin_offset_causal_matches_square, pin_offset_more_queries_than_keys,
               lambda: pin_finite_differences([(1, 3, 1, 2), (2, 5, 3, 4)])]
 
 
@@ -315,3 +411,28 @@ def test_mutants_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, FloatingPointError, RuntimeError):
             caught.append(getattr(pin, "__name__", "fd"))
     assert caught, f"mutant {name} passed every pin"
+
+
+# Planted mistakes in the merge of partial results.
+MERGE_MUTANTS = {
+    "merge_lse_without_log": ("m_safe + np.log(np.where(empty, 1.0, tot))",
+                              "m_safe + np.where(empty, 1.0, tot)"),
+    "merge_weights_unnormalised": ("wn = w / np.where(empty, 1.0, tot)[None]", "wn = w"),
+    "merge_first_part_only": ("w = np.exp(LSE_parts - m_safe[None])",
+                              "w = np.exp(LSE_parts[:1] - m_safe[None])"),
+    "merge_weights_without_exp": ("w = np.exp(LSE_parts - m_safe[None])",
+                                  "w = LSE_parts - m_safe[None]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_MUTANTS))
+def test_merge_mutants_are_caught(name, monkeypatch):
+    old, new = MERGE_MUTANTS[name]
+    src = inspect.getsource(oa.merge_partials)
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    ns = dict(vars(oa))
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oa, "merge_partials", ns["merge_partials"])
+    with pytest.raises((AssertionError, ValueError, FloatingPointError)):
+        with np.errstate(all="ignore"):
+            pin_merge_partials()
