@@ -91,6 +91,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            const fa_fwd_strides* strides, hipStream_t stream);
 
 /*
+ * fa_fwd_qk -- fa_fwd with Nq query rows against Nk keys (fa_fwd is the
+ * case Nq = Nk = N).
+ *   q, o : [B, Nq, H, D];  k, v : [B, Nk, H, D];  lse : [B, H, Nq].
+ *   causal = 1 aligns the mask to the last query and key: query i sees key j
+ *   iff j <= i + Nk - Nq.  So Nq new queries against an Nk-key history see
+ *   what the last Nq rows of the square problem see, and with Nq > Nk the
+ *   first Nq - Nk queries see no key: their o row is 0 and lse is -inf (the
+ *   logsumexp of an empty set).  The mask, and the exact merge of results
+ *   over split key sets (fa_merge), are those of the reading of the pages'
+ *   causal (lower-triangular) mask for unequal lengths.
+ * Other arguments, errors and memory: as fa_fwd (Nq and Nk both >= 1).
+ */
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int D, int causal, float scale,
+              int dtype, const fa_fwd_strides* strides, hipStream_t stream);
+
+/*
  * fa_bwd_workspace_bytes -- size of the scratch fa_bwd needs: the row vector
  * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
  * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]
@@ -99,6 +116,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
+
+/* Workspace of fa_bwd_qk: as above with Dvec and the dQ accumulator over Nq
+ * rows and the maxima over ceil(max(Nq, Nk) / 16) blocks. */
+size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
 
 /*
  * fa_bwd -- attention backward by recomputation.
@@ -149,10 +170,43 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
                   void* workspace, size_t workspace_bytes, unsigned stages,
                   hipStream_t stream);
 
+/*
+ * fa_bwd_qk -- fa_bwd_stages with Nq query rows against Nk keys, for o and
+ * lse from fa_fwd_qk with the same arguments.  q, o, dout, dq : [B, Nq, H,
+ * D]; k, v, dk, dv : [B, Nk, H, D]; lse : [B, H, Nq]; workspace of at least
+ * fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D) bytes.  Queries that see no
+ * key get dq = 0 and add nothing to dk, dv.  Stages, errors and memory: as
+ * fa_bwd_stages (FA_STAGE_ALL for the whole backward).
+ */
+int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int Nq, int Nk, int D, int causal, float scale,
+              int dtype, const fa_bwd_strides* strides, void* workspace,
+              size_t workspace_bytes, unsigned stages, hipStream_t stream);
+
+/*
+ * fa_merge -- exact combination of P attention results over disjoint key
+ * sets of the same queries (for example the chunks of a sequence-sharded or
+ * chunked K/V): LSE = ln sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r.
+ * This is what keeping the logsumexp allows (hotelren.com FlashAttention-2
+ * walkthrough, section 3.1).  Rows that no part covers (all LSE_r = -inf)
+ * get o = 0, lse = -inf.
+ *   o_parts   : device, P results stacked contiguously, [P, B, N, H, D], dtype.
+ *   lse_parts : device, fp32 [P, B, H, N].
+ *   o         : output, contiguous [B, N, H, D], dtype (must not overlap the
+ *               parts).
+ *   lse       : output, fp32 [B, H, N].
+ * The weights and sums are fp32; o is rounded once (RNE).  Errors: as
+ * fa_fwd (P <= 0: FA_ERR_INVALID_ARG).  Extra device memory: none.
+ */
+int fa_merge(const void* o_parts, const float* lse_parts, int P, void* o,
+             float* lse, int B, int H, int N, int D, int dtype,
+             hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(int status);
 
-/* Library version string, e.g. "fa-gfx950 0.1.0" (static string). */
+/* Library version string, e.g. "fa-gfx950 0.2.0" (static string). */
 const char* fa_version(void);
 
 #ifdef __cplusplus

@@ -5,7 +5,7 @@ this package is its thin Python binding.
 """
 
 from .attention import (FaArgError, bwd, flash_attn_func, flash_attn_qkvpacked_func, fwd,
-                        workspace_bytes)
+                        merge, workspace_bytes)
 
-__all__ = ["fwd", "bwd", "flash_attn_func", "flash_attn_qkvpacked_func", "workspace_bytes",
-           "FaArgError"]
+__all__ = ["fwd", "bwd", "merge", "flash_attn_func", "flash_attn_qkvpacked_func",
+           "workspace_bytes", "FaArgError"]

@@ -49,6 +49,24 @@ def _check_inputs(*tensors):
     return B, N, H, D
 
 
+def _check_qkv(q, k, v):
+    """q [B, Nq, H, D] against k, v [B, Nk, H, D]; returns (B, Nq, Nk, H, D)."""
+    for t in (q, k, v):
+        if t.dim() != 4:
+            raise FaArgError(f"expected [batch, seq, heads, head_dim] tensors, got {tuple(t.shape)}")
+    if k.shape != v.shape:
+        raise FaArgError(f"shape mismatch: {tuple(v.shape)} vs {tuple(k.shape)}")
+    if (q.shape[0], q.shape[2], q.shape[3]) != (k.shape[0], k.shape[2], k.shape[3]):
+        raise FaArgError(f"q {tuple(q.shape)} and k, v {tuple(k.shape)} differ in batch, heads "
+                         "or head_dim")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise FaArgError(f"dtype mismatch: {q.dtype}, {k.dtype}, {v.dtype}")
+    if q.device != k.device or q.device != v.device:
+        raise FaArgError(f"device mismatch: {q.device}, {k.device}, {v.device}")
+    B, Nq, H, D = _check_inputs(q)
+    return B, Nq, k.shape[1], H, D
+
+
 def _usable(t: torch.Tensor) -> torch.Tensor:
     """The kernels need d-stride 1, b/n/h strides that are multiples of 8
     elements and a 16-byte aligned base; copy otherwise."""
@@ -79,9 +97,11 @@ def _raise(status: int, what: str):
 
 
 def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
-    """Forward pass.  Returns (o [B,N,H,D], lse [B,H,N] fp32)."""
+    """Forward pass.  q [B,Nq,H,D], k and v [B,Nk,H,D] (Nk = Nq for
+    self-attention).  Returns (o [B,Nq,H,D], lse [B,H,Nq] fp32).  With
+    Nq != Nk the causal mask is aligned to the last query and key."""
     lib = _lib.load()
-    B, N, H, D = _check_inputs(q, k, v)
+    B, N, Nk, H, D = _check_qkv(q, k, v)
     q, k, v = _usable(q), _usable(k), _usable(v)
     if out is None:
         out = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
@@ -92,62 +112,91 @@ def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
     elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise FaArgError("lse must be a contiguous float32 [B, H, N] tensor")
     st = _lib.FwdStrides(_stride3(q), _stride3(k), _stride3(v), _stride3(out))
-    status = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                        lse.data_ptr(), B, H, N, D, int(bool(causal)),
-                        _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
-                        _stream(q))
+    status = lib.fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, H, N, Nk, D, int(bool(causal)),
+                           _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
+                           _stream(q))
     if status != _lib.FA_OK:
-        _raise(status, "fa_fwd")
+        _raise(status, "fa_fwd_qk")
     return out, lse
 
 
-def workspace_bytes(B: int, H: int, N: int, D: int) -> int:
-    return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, D))
+def workspace_bytes(B: int, H: int, N: int, D: int, Nk: int | None = None) -> int:
+    """Backward workspace for N query rows against Nk (default N) keys."""
+    return int(_lib.load().fa_bwd_qk_workspace_bytes(B, H, N, N if Nk is None else Nk, D))
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
         dq=None, dk=None, dv=None, workspace=None, stage_hook=None):
-    """Backward pass.  Returns (dq, dk, dv), each [B,N,H,D] in the input type.
+    """Backward pass.  Returns (dq [B,Nq,H,D], dk, dv [B,Nk,H,D]) in the
+    input type.
 
     ``stage_hook``: optional callable; when given, the three backward kernels
-    are enqueued one by one (fa_bwd_stages) and ``stage_hook(name)`` is called
-    before and after the dK/dV stage with name "dkdv_begin" / "dkdv_end"
-    (used to record stream events around that kernel).
+    are enqueued one by one and ``stage_hook(name)`` is called before and
+    after the dK/dV stage with name "dkdv_begin" / "dkdv_end" (used to record
+    stream events around that kernel).
     """
     lib = _lib.load()
-    B, N, H, D = _check_inputs(q, k, v, o, dout)
+    B, N, Nk, H, D = _check_qkv(q, k, v)
+    _check_inputs(q, o, dout)
     q, k, v, o, dout = (_usable(t) for t in (q, k, v, o, dout))
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise FaArgError("lse must be a contiguous float32 [B, H, N] tensor")
     if dq is None:
         dq = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
     if dk is None:
-        dk = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
+        dk = torch.empty((B, Nk, H, D), dtype=q.dtype, device=q.device)
     if dv is None:
-        dv = torch.empty((B, N, H, D), dtype=q.dtype, device=q.device)
-    _check_inputs(q, dq, dk, dv)
-    need = lib.fa_bwd_workspace_bytes(B, H, N, D)
+        dv = torch.empty((B, Nk, H, D), dtype=q.dtype, device=q.device)
+    _check_inputs(q, dq)
+    _check_inputs(k, dk, dv)
+    need = lib.fa_bwd_qk_workspace_bytes(B, H, N, Nk, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib.BwdStrides(*(_stride3(t) for t in (q, k, v, o, dout, dq, dk, dv)))
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D,
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, Nk, D,
             int(bool(causal)), _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
             workspace.data_ptr(), workspace.numel())
     if stage_hook is None:
-        status = lib.fa_bwd(*args, _stream(q))
+        status = lib.fa_bwd_qk(*args, _lib.STAGE_ALL, _stream(q))
         if status != _lib.FA_OK:
-            _raise(status, "fa_bwd")
+            _raise(status, "fa_bwd_qk")
         return dq, dk, dv
     for stage in (_lib.STAGE_PREPROCESS, _lib.STAGE_DKDV, _lib.STAGE_DQ):
         if stage == _lib.STAGE_DKDV:
             stage_hook("dkdv_begin")
-        status = lib.fa_bwd_stages(*args, stage, _stream(q))
+        status = lib.fa_bwd_qk(*args, stage, _stream(q))
         if status != _lib.FA_OK:
-            _raise(status, "fa_bwd_stages")
+            _raise(status, "fa_bwd_qk")
         if stage == _lib.STAGE_DKDV:
             stage_hook("dkdv_end")
     return dq, dk, dv
+
+
+def merge(o_parts, lse_parts):
+    """Exact merge of results over disjoint key sets (fa_merge).
+
+    o_parts [P, B, N, H, D] (dtype) and lse_parts [P, B, H, N] (fp32), for
+    example torch.stack of several fwd results.  Returns (o [B,N,H,D],
+    lse [B,H,N])."""
+    lib = _lib.load()
+    if o_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise FaArgError("expected o_parts [P, B, N, H, D] and lse_parts [P, B, H, N]")
+    P, B, N, H, D = o_parts.shape
+    if tuple(lse_parts.shape) != (P, B, H, N) or lse_parts.dtype != torch.float32:
+        raise FaArgError(f"lse_parts must be float32 [P, B, H, N] = {(P, B, H, N)}")
+    _check_inputs(o_parts[0])
+    if lse_parts.device != o_parts.device:
+        raise FaArgError("o_parts and lse_parts must be on one device")
+    o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
+    o = torch.empty((B, N, H, D), dtype=o_parts.dtype, device=o_parts.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    status = lib.fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), P, o.data_ptr(),
+                          lse.data_ptr(), B, H, N, D, _DTYPES[o_parts.dtype], _stream(o))
+    if status != _lib.FA_OK:
+        _raise(status, "fa_merge")
+    return o, lse
 
 
 class _FlashAttn(torch.autograd.Function):
@@ -187,7 +236,9 @@ class _FlashAttnQKVPacked(torch.autograd.Function):
 
 
 def flash_attn_func(q, k, v, causal: bool = False, softmax_scale=None):
-    """Exact attention on [B, N, H, D] tensors, differentiable."""
+    """Exact attention on [B, N, H, D] tensors, differentiable.  k and v may
+    have a different sequence length from q (causal mask aligned to the last
+    query and key)."""
     return _FlashAttn.apply(q, k, v, causal, softmax_scale)
 
 

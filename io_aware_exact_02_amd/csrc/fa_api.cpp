@@ -49,13 +49,36 @@ size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
 
 }  // namespace
 
+namespace {
+// Workspace layout of the backward, each part starting on a 256-byte
+// boundary: Dvec [B, H, Nq] fp32 | dQ accumulator [B, H, Nq, D] int32 |
+// bound maxima [B*H, 3, ceil(max(Nq, Nk) / 16)] fp32 | dQ bound [B*H] fp32.
+struct BwdWorkspace {
+  size_t dvec, dq, part, unit, total;
+};
+BwdWorkspace bwd_workspace(int B, int H, int Nq, int Nk, int D) {
+  const size_t heads = static_cast<size_t>(B) * H;
+  const size_t rows = heads * Nq;
+  const size_t nmax = static_cast<size_t>(Nq > Nk ? Nq : Nk);
+  BwdWorkspace w{};
+  w.dvec = 0;
+  w.dq = align256(rows * sizeof(float));
+  w.part = w.dq + align256(rows * D * sizeof(int32_t));
+  w.unit = w.part + align256(heads * 3 * ((nmax + 15) / 16) * sizeof(float));
+  w.total = w.unit + align256(heads * sizeof(float));
+  return w;
+}
+}  // namespace
+
 extern "C" {
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-           int N, int D, int causal, float scale, int dtype, const fa_fwd_strides* strides,
-           hipStream_t stream) {
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int D, int causal, float scale, int dtype,
+              const fa_fwd_strides* strides, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  int st = check_sizes(B, H, N, D, causal, scale, dtype);
+  int st = check_sizes(B, H, Nq, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_sizes(B, H, Nk, D, causal, scale, dtype);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_UNSUPPORTED;
@@ -71,15 +94,19 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     p.sv = from_abi(strides->v);
     p.so = from_abi(strides->o);
   } else {
-    p.sq = p.sk = p.sv = p.so = contiguous(N, H, D);
+    p.sq = p.so = contiguous(Nq, H, D);
+    p.sk = p.sv = contiguous(Nk, H, D);
   }
-  for (const fa::Strides* s : {&p.sq, &p.sk, &p.sv, &p.so}) {
-    st = check_strides(*s, B, N, H, D);
-    if (st != FA_OK) return st;
+  for (const fa::Strides* s : {&p.sq, &p.so}) {
+    if ((st = check_strides(*s, B, Nq, H, D)) != FA_OK) return st;
+  }
+  for (const fa::Strides* s : {&p.sk, &p.sv}) {
+    if ((st = check_strides(*s, B, Nk, H, D)) != FA_OK) return st;
   }
   p.B = B;
   p.H = H;
-  p.N = N;
+  p.N = Nq;
+  p.Nk = Nk;
   const float c = std::fabs(scale) * 1.4426950408889634f;
   p.c = c > 1e-30f ? c : 1e-30f;
   p.negate_q = scale < 0.0f ? 1 : 0;
@@ -87,44 +114,35 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-namespace {
-// Workspace layout of fa_bwd, each part starting on a 256-byte boundary:
-// Dvec [B, H, N] fp32 | dQ accumulator [B, H, N, D] int32 | bound maxima
-// [B*H, 3, ceil(N / 16)] fp32 | dQ bound [B*H] fp32.
-struct BwdWorkspace {
-  size_t dvec, dq, part, unit, total;
-};
-BwdWorkspace bwd_workspace(int B, int H, int N, int D) {
-  const size_t heads = static_cast<size_t>(B) * H;
-  const size_t rows = heads * N;
-  BwdWorkspace w{};
-  w.dvec = 0;
-  w.dq = align256(rows * sizeof(float));
-  w.part = w.dq + align256(rows * D * sizeof(int32_t));
-  w.unit = w.part + align256(heads * 3 * ((static_cast<size_t>(N) + 15) / 16) * sizeof(float));
-  w.total = w.unit + align256(heads * sizeof(float));
-  return w;
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+           int N, int D, int causal, float scale, int dtype, const fa_fwd_strides* strides,
+           hipStream_t stream) {
+  return fa_fwd_qk(q, k, v, o, lse, B, H, N, N, D, causal, scale, dtype, strides, stream);
 }
-}  // namespace
+
+size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || D <= 0) return 0;
+  return bwd_workspace(B, H, Nq, Nk, D).total;
+}
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D) {
-  if (B <= 0 || H <= 0 || N <= 0 || D <= 0) return 0;
-  return bwd_workspace(B, H, N, D).total;
+  return fa_bwd_qk_workspace_bytes(B, H, N, N, D);
 }
 
-int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
-                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
-                  int H, int N, int D, int causal, float scale, int dtype,
-                  const fa_bwd_strides* strides, void* workspace, size_t workspace_bytes,
-                  unsigned stages, hipStream_t stream) {
+int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+              int D, int causal, float scale, int dtype, const fa_bwd_strides* strides,
+              void* workspace, size_t workspace_bytes, unsigned stages, hipStream_t stream) {
   if (stages == 0 || (stages & ~FA_STAGE_ALL) != 0) return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
     return FA_ERR_INVALID_ARG;
-  int st = check_sizes(B, H, N, D, causal, scale, dtype);
+  int st = check_sizes(B, H, Nq, D, causal, scale, dtype);
   if (st != FA_OK) return st;
-  // One head's dQ accumulator is addressed as a buffer of N*D*4 bytes.
-  if (static_cast<int64_t>(N) * D * 4 > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
-  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, D)) return FA_ERR_INVALID_ARG;
+  st = check_sizes(B, H, Nk, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  // One head's dQ accumulator is addressed as a buffer of Nq*D*4 bytes.
+  if (static_cast<int64_t>(Nq) * D * 4 > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D)) return FA_ERR_INVALID_ARG;
   for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq),
                           static_cast<const void*>(dk), static_cast<const void*>(dv)}) {
     if (!aligned16(ptr)) return FA_ERR_UNSUPPORTED;
@@ -151,13 +169,16 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
     p.sdk = from_abi(strides->dk);
     p.sdv = from_abi(strides->dv);
   } else {
-    p.sq = p.sk = p.sv = p.so = p.sdo = p.sdq = p.sdk = p.sdv = contiguous(N, H, D);
+    p.sq = p.so = p.sdo = p.sdq = contiguous(Nq, H, D);
+    p.sk = p.sv = p.sdk = p.sdv = contiguous(Nk, H, D);
   }
-  for (const fa::Strides* s : {&p.sq, &p.sk, &p.sv, &p.so, &p.sdo, &p.sdq, &p.sdk, &p.sdv}) {
-    st = check_strides(*s, B, N, H, D);
-    if (st != FA_OK) return st;
+  for (const fa::Strides* s : {&p.sq, &p.so, &p.sdo, &p.sdq}) {
+    if ((st = check_strides(*s, B, Nq, H, D)) != FA_OK) return st;
   }
-  const BwdWorkspace w = bwd_workspace(B, H, N, D);
+  for (const fa::Strides* s : {&p.sk, &p.sv, &p.sdk, &p.sdv}) {
+    if ((st = check_strides(*s, B, Nk, H, D)) != FA_OK) return st;
+  }
+  const BwdWorkspace w = bwd_workspace(B, H, Nq, Nk, D);
   char* ws = static_cast<char*>(workspace);
   p.dvec = reinterpret_cast<float*>(ws + w.dvec);
   p.dq_fix = reinterpret_cast<int32_t*>(ws + w.dq);
@@ -165,19 +186,52 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
   p.dq_bound = reinterpret_cast<float*>(ws + w.unit);
   p.B = B;
   p.H = H;
-  p.N = N;
+  p.N = Nq;
+  p.Nk = Nk;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_bwd(p, dtype, D, causal, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                  int H, int N, int D, int causal, float scale, int dtype,
+                  const fa_bwd_strides* strides, void* workspace, size_t workspace_bytes,
+                  unsigned stages, hipStream_t stream) {
+  return fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, N, D, causal, scale, dtype,
+                   strides, workspace, workspace_bytes, stages, stream);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int D,
            int causal, float scale, int dtype, const fa_bwd_strides* strides, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
-  return fa_bwd_stages(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, D, causal, scale, dtype,
-                       strides, workspace, workspace_bytes, FA_STAGE_ALL, stream);
+  return fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, N, D, causal, scale, dtype,
+                   strides, workspace, workspace_bytes, FA_STAGE_ALL, stream);
+}
+
+int fa_merge(const void* o_parts, const float* lse_parts, int P, void* o, float* lse, int B,
+             int H, int N, int D, int dtype, hipStream_t stream) {
+  if (!o_parts || !lse_parts || !o || !lse || P <= 0) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, N, D, 0, 1.0f, dtype);
+  if (st != FA_OK) return st;
+  if (static_cast<int64_t>(P) * B * H * N * D > kI64Max / 8) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(o_parts) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(lse_parts) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return FA_ERR_UNSUPPORTED;
+  fa::MergeParams p{};
+  p.o_parts = static_cast<const uint16_t*>(o_parts);
+  p.lse_parts = lse_parts;
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.P = P;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  const hipError_t e = fa::launch_merge(p, dtype, D, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_status_str(int status) {
@@ -190,6 +244,6 @@ const char* fa_status_str(int status) {
   }
 }
 
-const char* fa_version(void) { return "fa-gfx950 0.1.0"; }
+const char* fa_version(void) { return "fa-gfx950 0.2.0"; }
 
 }  // extern "C"

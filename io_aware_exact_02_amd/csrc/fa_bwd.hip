@@ -39,8 +39,9 @@
 namespace fa {
 
 // ------------------------------------------------------------------ kernel 1
-// Grid (ceil(N / RPB), B*H): each workgroup covers RPB rows of one head and
-// records the largest |dO|, |K| and |V| elements of those rows.
+// Grid (ceil(max(N, Nk) / RPB), B*H): each workgroup covers RPB query and
+// key rows of one head and records the largest |dO|, |K| and |V| elements of
+// those rows.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   constexpr int TPR = D / 8;       // threads per row (8 elements each)
@@ -52,20 +53,22 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   const int n = static_cast<int>(blockIdx.x) * RPB + tid / TPR;
   const int64_t row = static_cast<int64_t>(bh) * p.N + n;
   float s = 0.0f, domax = 0.0f, vmax = 0.0f, kmax = 0.0f;
-  if (n < p.N) {
-    const int64_t nn = n;
+  const int64_t nn = n;
+  if (n < p.N) {  // query row n
     const u32x4 o = ldg16(p.o + b * p.so.b + nn * p.so.n + h * p.so.h + part * 8);
     const u32x4 d = ldg16(p.dout + b * p.sdo.b + nn * p.sdo.n + h * p.sdo.h + part * 8);
-    const u32x4 k = ldg16(p.k + b * p.sk.b + nn * p.sk.n + h * p.sk.h + part * 8);
-    const u32x4 v = ldg16(p.v + b * p.sv.b + nn * p.sv.n + h * p.sv.h + part * 8);
     s = dot8<T>(o, d);
     domax = absmax8<T>(d);
-    vmax = absmax8<T>(v);
-    kmax = absmax8<T>(k);
     int32_t* acc = p.dq_fix + row * D + part * 8;
     const u32x4 z = {0u, 0u, 0u, 0u};
     stg16(acc, z);
     stg16(acc + 4, z);
+  }
+  if (n < p.Nk) {  // key row n
+    const u32x4 k = ldg16(p.k + b * p.sk.b + nn * p.sk.n + h * p.sk.h + part * 8);
+    const u32x4 v = ldg16(p.v + b * p.sv.b + nn * p.sv.n + h * p.sv.h + part * 8);
+    vmax = absmax8<T>(v);
+    kmax = absmax8<T>(k);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
@@ -159,7 +162,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int kblk = static_cast<int>(blockIdx.x / BH);
   const int b = bh / p.H;
   const int h = bh % p.H;
-  const int N = p.N;
+  const int N = p.N;    // query rows
+  const int Nk = p.Nk;  // keys; causal: query i sees keys j <= i + off
+  const int off = Nk - N;
   const float c_scale = p.c;
 
   const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (key < N) {
+    if (key < Nk) {
       if constexpr (!KLDS) kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + 16 * kc + 8 * hh);
       vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + 16 * kc + 8 * hh);
     }
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     const int col = (c % CPR) * 8;
     const int kk = kb0 + row;
     u32x4 kv = {0u, 0u, 0u, 0u};
-    if (kk < N) kv = ldg16(kbase + static_cast<int64_t>(kk) * p.sk.n + col);
+    if (kk < Nk) kv = ldg16(kbase + static_cast<int64_t>(kk) * p.sk.n + col);
     lds_write16(&Ks[tile_off<D>(row, col)], kv);
   }
 
@@ -263,7 +268,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // ---- next-tile staging: global pointers, LDS offsets, registers
-  const int q_begin = CAUSAL ? kb0 : 0;
+  // Causal: the first query that sees the workgroup's first key (the last
+  // query sees every key, so at least one tile remains).
+  const int q_begin = CAUSAL ? max(kb0 - off, 0) : 0;
   const int ntiles = (N - q_begin + BQ - 1) / BQ;
   const uint16_t* qptr[QPT];
   const uint16_t* doptr[QPT];
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
         float pr = __builtin_amdgcn_exp2f(fmaf(s[i], c_scale, -lv[i]));
         if constexpr (MASK) {
           const int q = qt + 32 * qb + c_item(i, hh);
-          const bool valid = key < N && (!CAUSAL || key <= q);
+          const bool valid = key < Nk && (!CAUSAL || key <= q + off);
           pr = valid ? pr : 0.0f;
         }
         pv[i] = pr;
@@ -433,8 +440,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     if (t > 0) dq_atomics(qt - BQ);
 
     u32x4 pS[NQB][2];
-    if (!CAUSAL || qt + BQ - 1 >= kw0) {
-      const bool need_mask = (CAUSAL && kw0 + 31 > qt) || (kw0 + 31 >= N);
+    if (!CAUSAL || qt + BQ - 1 + off >= kw0) {
+      const bool need_mask = (CAUSAL && kw0 + 31 > qt + off) || (kw0 + 31 >= Nk);
       if (need_mask) {
         compute(bufc, IntC<1>{}, qt, pS);
       } else {
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     step(IntC<0>{}, t);
     if (t + 1 < ntiles) step(IntC<1>{}, t + 1);
   }
-  dq_atomics(q_begin + (ntiles - 1) * BQ);
+  if (ntiles > 0) dq_atomics(q_begin + (ntiles - 1) * BQ);
 
   // Epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO.  C value i: key
   // kw0 + c_row(i, hh), d = 32*db + l32.
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk = kw0 + c_row(i, hh);
-      if (kk < N) {
+      if (kk < Nk) {
         const int d = 32 * db + l32;
         p.dk[b * p.sdk.b + static_cast<int64_t>(kk) * p.sdk.n + h * p.sdk.h + d] =
             to_half_bits<T>(dkacc[db][i] * p.scale);
@@ -540,9 +547,9 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   using Sh = BwdShape<D>;
   constexpr int NW = Sh::NW;
   BwdParams p = p_in;
-  p.num_kblocks = (p.N + BwdCfg<D, NW, Sh::BQ>::BKV - 1) / BwdCfg<D, NW, Sh::BQ>::BKV;
+  p.num_kblocks = (p.Nk + BwdCfg<D, NW, Sh::BQ>::BKV - 1) / BwdCfg<D, NW, Sh::BQ>::BKV;
   constexpr int RPB = 256 / (D / 8);
-  p.npart = (p.N + RPB - 1) / RPB;
+  p.npart = (max(p.N, p.Nk) + RPB - 1) / RPB;
   const dim3 row_grid(static_cast<unsigned>(p.npart), static_cast<unsigned>(p.B * p.H));
   hipError_t e = hipSuccess;
   if (stages & 1u) {

@@ -82,7 +82,9 @@ void fwd_kernel(FwdParams p) {
   const int qblk = p.num_qblocks - 1 - static_cast<int>(blockIdx.x / BH);  // heaviest first
   const int b = bh / p.H;
   const int h = bh % p.H;
-  const int N = p.N;
+  const int N = p.N;    // query rows
+  const int Nk = p.Nk;  // keys; causal: query i sees keys j <= i + off
+  const int off = Nk - N;
 
   const int q0 = qblk * BR + wave * 32;  // first query row of this wave
   const int qrow = q0 + l32;             // the query row this lane serves
@@ -135,7 +137,9 @@ void fwd_kernel(FwdParams p) {
   const float c_scale = p.c;
 
   const int qlast = min(qblk * BR + BR, N) - 1;
-  const int ntiles = CAUSAL ? (qlast / BC + 1) : ((N + BC - 1) / BC);
+  // Causal: up to the last key the workgroup's last row sees (at least one
+  // tile, so that rows seeing no key still go through the masked path).
+  const int ntiles = CAUSAL ? (max(min(qlast + off, Nk - 1), 0) / BC + 1) : ((Nk + BC - 1) / BC);
 
   // Issue the loads of tile j into buffer BUF.  Rows past N (last tile only)
   // are clamped to row N-1: those keys are masked, so their finite values
@@ -145,12 +149,12 @@ void fwd_kernel(FwdParams p) {
     const int kv0 = j * BC;
     const uint16_t* kt = kbase + static_cast<int64_t>(kv0) * p.sk.n;
     const uint16_t* vt = vbase + static_cast<int64_t>(kv0) * p.sv.n;
-    const bool tail = kv0 + BC > N;
+    const bool tail = kv0 + BC > Nk;
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
       uint32_t ko = gk_off[it], vo = gv_off[it];
       if (tail) {
-        const int last = N - 1 - kv0;
+        const int last = Nk - 1 - kv0;
         const int slot = (wave + NW * it) * 64 + lane;
         const int pr = slot / CPR;
         const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;
@@ -190,7 +194,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kv0 + 32 * nb + c_item(i, hh);
-          if (key >= N || (CAUSAL && key > qrow)) acc[i] = -INFINITY;
+          if (key >= Nk || (CAUSAL && key > qrow + off)) acc[i] = -INFINITY;
         }
       }
     };
@@ -205,7 +209,9 @@ void fwd_kernel(FwdParams p) {
     auto soft_half = [&](const f32x16& acc, u32x4 (&pbh)[2]) {
       float lt, lbt;
       auto weights = [&]() {
-        const float negm = -m;
+        // m = -inf (no key seen yet): a huge finite shift instead, so that
+        // visible keys overflow the sum (and move m) while masked ones give 0.
+        const float negm = -fmaxf(m, -3.0e38f);
         float pv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c_scale, negm));
@@ -237,7 +243,8 @@ void fwd_kernel(FwdParams p) {
           mx1 = fmaxf(mx1, acc[i + 1]);
         }
         const float mnew = fmaxf(m, max_xor32(fmaxf(mx0, mx1)) * c_scale);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        // m == mnew also covers lanes that have seen no key (both -inf).
+        const float alpha = m == mnew ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
         l *= alpha;
         lb *= alpha;
 #pragma unroll
@@ -275,8 +282,8 @@ void fwd_kernel(FwdParams p) {
     const int kv0 = j * BC;
     if (j + 1 < ntiles) load_tile(IntC<BUF ^ 1>{}, j + 1);
     // Causal: tiles entirely above this wave's rows carry no weight for it.
-    if (!CAUSAL || kv0 <= q0 + 31) {
-      const bool need_mask = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > q0);
+    if (!CAUSAL || kv0 <= q0 + 31 + off) {
+      const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + off);
       if (need_mask) {
         compute(bufc, IntC<1>{}, kv0);
       } else {
@@ -297,8 +304,11 @@ void fwd_kernel(FwdParams p) {
   // O is normalised by the sum of the weights exactly as the PV product used
   // them (rounded to the input type), so each output row is a convex
   // combination of V rows; the LSE uses the unrounded fp32 sum.
+  // A row that saw no key (possible only when N_q > N_k) has l = 0: O = 0,
+  // LSE = -inf.
   const float lt = sum_xor32(l);
-  const float inv = __builtin_amdgcn_rcpf(sum_xor32(lb));
+  const float lbs = sum_xor32(lb);
+  const float inv = lbs > 0.0f ? __builtin_amdgcn_rcpf(lbs) : 0.0f;
   if (qrow < N) {
     uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
 #pragma unroll

@@ -17,7 +17,8 @@ struct FwdParams {
   uint16_t* o;
   float* lse;  // [B, H, N] fp32
   Strides sq, sk, sv, so;
-  int B, H, N;
+  int B, H, N;      // N: query rows
+  int Nk;           // keys (causal: query i sees keys j <= i + Nk - N)
   int num_qblocks;  // ceil(N / rows per workgroup)
   float c;          // |scale| * log2(e), at least 1e-30
   int negate_q;     // 1 when scale < 0: q enters the scores negated
@@ -38,11 +39,21 @@ struct BwdParams {
   float* bound_part;  // workspace: [B*H, 3, npart] maxima per row block
   float* dq_bound;    // workspace: [B*H] dQ bound B; one fixed-point unit = B / 2^30
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
-  int B, H, N;
-  int num_kblocks;  // ceil(N / keys per workgroup)
+  int B, H, N;      // N: query rows
+  int Nk;           // keys (causal: query i sees keys j <= i + Nk - N)
+  int num_kblocks;  // ceil(Nk / keys per workgroup)
   int npart;        // row blocks per head in bound_part
   float scale;
   float c;  // scale * log2(e)
+};
+
+// Exact merge of partial attention results (see fa_merge in fa.h).
+struct MergeParams {
+  const uint16_t* o_parts;  // [P, B, N, H, D] contiguous
+  const float* lse_parts;   // [P, B, H, N]
+  uint16_t* o;              // [B, N, H, D] contiguous
+  float* lse;               // [B, H, N]
+  int P, B, H, N;
 };
 
 // dtype: 0 = f16, 1 = bf16.  Return the launch status.
@@ -50,5 +61,6 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStrea
 // stages: bit 0 preprocess, bit 1 dK/dV (+ dQ accumulation), bit 2 dQ conversion.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
                       hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s);
 
 }  // namespace fa

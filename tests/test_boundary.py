@@ -152,3 +152,74 @@ def test_python_binding_rejects_bad_inputs_without_gpu():
         fa._check_inputs(x, x, x)
     with pytest.raises(fa.FaArgError, match=r"\[B, N, 3, H, D\]"):
         fa.flash_attn_qkvpacked_func(torch.zeros(1, 16, 2, 2, 64, dtype=torch.float16))
+
+
+def test_unequal_length_entry_points_reject_before_launch():
+    lib = _lib.load()
+
+    def fwd_qk(Nq=128, Nk=256, **kw):
+        a = dict(ARGS_OK, **kw)
+        return lib.fa_fwd_qk(P, P, P, P, P, a["B"], a["H"], Nq, Nk, a["D"], a["causal"],
+                             a["scale"], a["dtype"], None, None)
+
+    assert fwd_qk(Nq=0) == _lib.FA_ERR_INVALID_ARG
+    assert fwd_qk(Nk=0) == _lib.FA_ERR_INVALID_ARG
+    assert fwd_qk(Nk=-5) == _lib.FA_ERR_INVALID_ARG
+    assert fwd_qk(D=48) == _lib.FA_ERR_UNSUPPORTED
+    assert fwd_qk(causal=3) == _lib.FA_ERR_INVALID_ARG
+    # strides are checked against each tensor's own length
+    good_q, good_k = _lib.Stride3(128 * 64, 64, 64), _lib.Stride3(256 * 64, 64, 64)
+    s = _lib.FwdStrides(good_q, good_k, good_k, good_q)
+    s.k = _lib.Stride3(256 * 64, 66, 64)
+    assert lib.fa_fwd_qk(P, P, P, P, P, 1, 1, 128, 256, 64, 0, 0.125, _lib.FA_BF16,
+                         ctypes.byref(s), None) == _lib.FA_ERR_UNSUPPORTED
+
+    need = lib.fa_bwd_qk_workspace_bytes(1, 1, 128, 256, 64)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert need == (a256(4 * 128) + a256(4 * 128 * 64) + a256(4 * 3 * (256 // 16)) + a256(4))
+    assert lib.fa_bwd_qk_workspace_bytes(1, 1, 0, 256, 64) == 0
+    assert lib.fa_bwd_qk_workspace_bytes(1, 1, 5, 5, 64) == lib.fa_bwd_workspace_bytes(1, 1, 5, 64)
+
+    def bwd_qk(ws_bytes=1 << 40, stages=_lib.STAGE_ALL, Nq=128, Nk=256, **kw):
+        a = dict(ARGS_OK, **kw)
+        return lib.fa_bwd_qk(*([P] * 9), a["B"], a["H"], Nq, Nk, a["D"], a["causal"],
+                             a["scale"], a["dtype"], None, P, ws_bytes, stages, None)
+
+    assert bwd_qk(ws_bytes=need - 1) == _lib.FA_ERR_INVALID_ARG
+    assert bwd_qk(Nk=0) == _lib.FA_ERR_INVALID_ARG
+    assert bwd_qk(stages=0) == _lib.FA_ERR_INVALID_ARG
+    assert bwd_qk(stages=16) == _lib.FA_ERR_INVALID_ARG
+    # one head's dQ accumulator must stay below 2^31 bytes
+    assert bwd_qk(Nq=1 << 23, Nk=8, D=64) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_merge_rejects_before_launch():
+    lib = _lib.load()
+
+    def merge(o_parts=P, lse_parts=P, n=3, o=P, lse=P, B=1, H=2, N=64, D=64,
+              dtype=_lib.FA_BF16):
+        return lib.fa_merge(o_parts, lse_parts, n, o, lse, B, H, N, D, dtype, None)
+
+    assert merge(n=0) == _lib.FA_ERR_INVALID_ARG
+    assert merge(o_parts=None) == _lib.FA_ERR_INVALID_ARG
+    assert merge(lse=None) == _lib.FA_ERR_INVALID_ARG
+    assert merge(N=0) == _lib.FA_ERR_INVALID_ARG
+    assert merge(dtype=5) == _lib.FA_ERR_INVALID_ARG
+    assert merge(D=100) == _lib.FA_ERR_UNSUPPORTED
+    assert merge(o=P + 8) == _lib.FA_ERR_UNSUPPORTED
+    assert merge(lse_parts=P + 2) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_python_binding_checks_unequal_lengths_without_gpu():
+    q = torch.zeros(1, 16, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 40, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaArgError, match="GPU"):
+        fa.fwd(q, k, k)                       # lengths accepted, device rejected
+    with pytest.raises(fa.FaArgError, match="differ"):
+        fa.fwd(q, torch.zeros(1, 40, 3, 64, dtype=torch.bfloat16),
+               torch.zeros(1, 40, 3, 64, dtype=torch.bfloat16))
+    with pytest.raises(fa.FaArgError, match="shape mismatch"):
+        fa.fwd(q, k, torch.zeros(1, 41, 2, 64, dtype=torch.bfloat16))
+    with pytest.raises(fa.FaArgError, match="lse_parts"):
+        fa.merge(torch.zeros(2, 1, 16, 2, 64, dtype=torch.bfloat16),
+                 torch.zeros(2, 1, 2, 17, dtype=torch.float32))

@@ -216,6 +216,113 @@ def test_pages_sweep_shapes(name):
         assert_grad("dV", got["dV"][b, :, h], dV[b, :, h], f"{name} b{b} h{h}")
 
 
+# ------------------------------------------------ unequal lengths and merge
+
+def _qk_inputs(B, Nq, Nk, H, D, dtype, seed):
+    a = random_qkv(B, Nq, H, D, dtype, seed)
+    b = random_qkv(B, Nk, H, D, dtype, seed + 1)
+    return {"q": a["q"], "do": a["do"], "k": b["k"], "v": b["v"]}
+
+
+def _assert_forward_with_empty_rows(o, lse, O, LSE, what):
+    """Rows that see no key must come out exactly O = 0, LSE = -inf."""
+    empty = np.isneginf(LSE)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what} empty rows differ"
+    if empty.any():
+        e_rows = np.transpose(empty, (0, 2, 1))        # [B, N, H]
+        assert np.all(o[e_rows] == 0.0), f"{what} empty rows not zero"
+    assert np.all(np.isfinite(o)), what
+    assert np.max(np.abs(o - O)) <= O_TOL, f"{what} O"
+    if (~empty).any():
+        assert np.max(np.abs(lse[~empty] - LSE[~empty])) <= LSE_TOL, f"{what} LSE"
+
+
+QK_LENGTHS = [(1, 128), (64, 300), (300, 64), (17, 129), (128, 1000), (1000, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Nq,Nk", QK_LENGTHS)
+def test_unequal_lengths(Nq, Nk, D, causal, dtype):
+    """N_q != N_k, the causal mask aligned to the last query and key."""
+    what = f"Nq={Nq} Nk={Nk} D={D} causal={causal} {dtype}"
+    _say("case", what)
+    inp = _qk_inputs(2, Nq, Nk, 3, D, dtype, 7400 + Nq + Nk + D)
+    dev = torch.device("cuda")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.to("cpu", torch.float64).numpy()
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=causal)
+    _assert_forward_with_empty_rows(f64(o), f64(lse), O, LSE, what)
+    dQ, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=causal)
+    for name, got, ref in (("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+        assert got.shape == ref.shape
+        assert_grad(name, f64(got), ref, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_merge_of_key_chunks(D, dtype):
+    """Key sets split into chunks, attended separately and merged through
+    the LSE equal attention over all keys: three non-causal chunks; a causal
+    history split into its fully visible part and the causal rest; a part in
+    which the first rows see no key."""
+    _say("case merge", D, dtype)
+    dev = torch.device("cuda")
+    f64 = lambda t: t.to("cpu", torch.float64).numpy()
+    inp = _qk_inputs(2, 200, 700, 3, D, dtype, 7500 + D)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    cuts = [0, 250, 500, 700]
+    parts = [fa.fwd(q, k[:, a:b], v[:, a:b]) for a, b in zip(cuts, cuts[1:])]
+    o, lse = fa.merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]))
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"])
+    _assert_forward_with_empty_rows(f64(o), f64(lse), O, LSE, "3 chunks")
+    # causal: 200 queries after a 500-key history; keys [0, 384) are seen by all
+    s = 384
+    p0 = fa.fwd(q, k[:, :s], v[:, :s], causal=False)
+    p1 = fa.fwd(q, k[:, s:], v[:, s:], causal=True)
+    o, lse = fa.merge(torch.stack([p0[0], p1[0]]), torch.stack([p0[1], p1[1]]))
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=True)
+    _assert_forward_with_empty_rows(f64(o), f64(lse), O, LSE, "causal history")
+    # a causal part over 50 keys leaves the first 150 of the 200 rows empty
+    p2 = fa.fwd(q, k[:, :50], v[:, :50], causal=True)
+    p3 = fa.fwd(q, k[:, 50:], v[:, 50:], causal=False)
+    o, lse = fa.merge(torch.stack([p2[0], p3[0]]), torch.stack([p2[1], p3[1]]))
+    assert np.all(np.isneginf(f64(p2[1])[:, :, :150]))
+    parts_ref = [oa.attention_forward(inp["q"], inp["k"][:, :50], inp["v"][:, :50], causal=True),
+                 oa.attention_forward(inp["q"], inp["k"][:, 50:], inp["v"][:, 50:])]
+    O, LSE = oa.merge_partials(np.stack([p[0] for p in parts_ref]),
+                               np.stack([p[1] for p in parts_ref]))
+    _assert_forward_with_empty_rows(f64(o), f64(lse), O, LSE, "empty rows in a part")
+
+
+def test_chunked_prefill_matches_square():
+    """New queries against the whole history (N_q < N_k, causal) give the
+    same rows as the square causal problem, forward and dQ."""
+    _say("case chunked prefill")
+    dev = torch.device("cuda")
+    inp = random_qkv(1, 700, 4, 64, "bf16", seed=7600)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o_full, lse_full = fa.fwd(q, k, v, causal=True)
+    o_tail, lse_tail = fa.fwd(q[:, 500:], k, v, causal=True)
+    torch.cuda.synchronize()
+    # the same rows, grouped differently into waves: equal up to rounding
+    assert float(torch.max(torch.abs(lse_tail - lse_full[:, :, 500:]))) <= 1e-5
+    assert float(torch.max(torch.abs(o_tail.float() - o_full[:, 500:].float()))) <= 2.0 ** -6
+    do_tail = do.clone()
+    do_tail[:, :500] = 0
+    dq_full, dk_full, dv_full = fa.bwd(q, k, v, o_full, lse_full, do_tail, causal=True)
+    dq_t, dk_t, dv_t = fa.bwd(q[:, 500:], k, v, o_tail, lse_tail, do[:, 500:].contiguous(),
+                              causal=True)
+    torch.cuda.synchronize()
+    for a, b in ((dq_t, dq_full[:, 500:]), (dk_t, dk_full), (dv_t, dv_full)):
+        scale = float(torch.max(torch.abs(b.float())))
+        assert float(torch.max(torch.abs(a.float() - b.float()))) <= 2e-2 * scale
+
+
 # ------------------------------------------------------------ properties
 
 def test_determinism():
