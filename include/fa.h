@@ -140,7 +140,8 @@ size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
  * max|K| max|V| per (batch, head) -- a bound on any partial sum of dS K
  * -- and the dQ conversion.  The integer sum is exact, so dq is bitwise
  * reproducible; each key block's contribution is rounded to the nearest
- * unit.  Heads whose bound is not a finite normal float get dq = 0.
+ * unit.  B is raised to at least 2^-96 (the scale 2^30 / B stays finite);
+ * heads whose bound is not finite (non-finite inputs) get dq = 0.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,
