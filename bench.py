@@ -25,7 +25,12 @@ Prints ONE JSON line.  Besides the headline value it carries
                  PyTorch baseline at c3 (untimed pass);
   pages_sweep  : the pages' own forward speed comparison (standard fp16
                  attention vs the fused kernel, B=2 H=8 D=64 fp16 at
-                 N = 2048/4096/8192, causal at 4096), untimed by the step.
+                 N = 2048/4096/8192, causal at 4096), untimed by the step;
+  mha_layer    : forward + backward of the whole multi-head attention layer
+                 (QKV projection, attention, output projection) with the
+                 fused kernels against the same layer with standard fp16
+                 attention, B=2 N=2048 embed 768, 12 heads, untimed by the
+                 step.
 """
 
 from __future__ import annotations
@@ -216,6 +221,59 @@ def pages_sweep(torch, fa):
             "causal_vs_noncausal_fused_speedup_N4096": round(fused_ms["s4096"] / fused_ms["s4096c"], 2)}
 
 
+def mha_layer(torch, fa):
+    """Training step of the multi-head attention layer (forward and backward
+    of FlashMHA, random-init fp16 weights) at B=2, N=2048, embed 768, 12
+    heads, against the same layer and weights with the attention step done
+    the standard way (S and P materialised in fp16, autograd backward)."""
+    dev = torch.device("cuda")
+    B, N, E, H = 2, 2048, 768, 12
+    D = E // H
+    dt = torch.float16
+    torch.manual_seed(7300)
+    m = fa.FlashMHA(E, H, dtype=dt).to(dev)
+    gen = torch.Generator("cpu").manual_seed(7301)
+    x = torch.randn((B, N, E), generator=gen).to(dt).to(dev).requires_grad_(True)
+    dy = torch.randn((B, N, E), generator=gen).to(dt).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def standard_layer():
+        qkv = m.Wqkv(x).view(B, N, 3, H, D).permute(2, 0, 3, 1, 4)
+        q, k, v = (t.contiguous() for t in qkv.unbind(0))
+        s = torch.matmul(q, k.transpose(-2, -1).contiguous()) / (D ** 0.5)
+        o = torch.matmul(torch.softmax(s, dim=-1), v)
+        return m.out_proj(o.transpose(1, 2).reshape(B, N, E))
+
+    def train_step(layer):
+        m.zero_grad(set_to_none=True)
+        x.grad = None
+        layer().backward(dy)
+
+    def timed(layer, iters=10, warm=3):
+        for _ in range(warm):
+            train_step(layer)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(iters):
+            train_step(layer)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    t_fa = timed(lambda: m(x))
+    t_std = timed(standard_layer)
+    with torch.no_grad():
+        diff = float((m(x).float() - standard_layer().float()).abs().max())
+    del x, dy
+    torch.cuda.empty_cache()
+    return {"shape": f"B={B} N={N} embed={E} heads={H} head_dim={D} fp16 non-causal",
+            "fused_ms": round(t_fa, 4), "standard_ms": round(t_std, 4),
+            "speedup": round(t_std / t_fa, 2),
+            "fused_tokens_per_s": round(B * N / (t_fa * 1e-3)),
+            "max_output_diff": diff}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +285,7 @@ def main(argv=None):
     ap.add_argument("--no-memory", action="store_true", help="skip the c3 memory comparison")
     ap.add_argument("--no-pages-sweep", action="store_true",
                     help="skip the standard-vs-fused forward sweep of the pages (N=2048..8192)")
+    ap.add_argument("--no-mha", action="store_true", help="skip the attention-layer measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise kernel that reads and "
                          "writes this many MiB (calibrates HBM byte counters)")
@@ -353,6 +412,10 @@ def main(argv=None):
     if not args.no_pages_sweep:
         sweep = pages_sweep(torch, fa)
 
+    layer = None
+    if not args.no_mha:
+        layer = mha_layer(torch, fa)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(args.cpu_seconds)
@@ -381,6 +444,7 @@ def main(argv=None):
         "per_config": per_config,
         "memory_c3": memory,
         "pages_sweep": sweep,
+        "mha_layer": layer,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -77,7 +77,7 @@ def run(cmd, timeout, log):
 
 def bench_cmd(workloads, steps, calib_mib):
     return [sys.executable, BENCH, "--steps", str(steps), "--warmup", "2", "--cpu-seconds", "0",
-            "--no-memory", "--no-pages-sweep", "--workloads", workloads,
+            "--no-memory", "--no-pages-sweep", "--no-mha", "--workloads", workloads,
             "--copy-calibration-mib", str(calib_mib)]
 
 
@@ -159,7 +159,7 @@ def main(argv=None):
              "command: python -m io_aware_exact_02_amd.rocprof_harness --raw <dir> "
              f"--workloads {a.workloads} --steps {a.steps} --calib-mib {a.calib_mib}",
              "  runs: rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py "
-             f"--steps {a.steps} --warmup 2 --cpu-seconds 0 --no-memory --no-pages-sweep "
+             f"--steps {a.steps} --warmup 2 --cpu-seconds 0 --no-memory --no-pages-sweep --no-mha "
              f"--workloads {a.workloads} "
              f"--copy-calibration-mib {a.calib_mib}",
              "        and the same command under rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
