@@ -24,15 +24,30 @@
 // transposing LDS reads.  K/V tiles of 64 keys are double-buffered: the next
 // tile is copied global -> LDS asynchronously while the current one is
 // consumed, so there is one barrier per tile.
+//
+// Causal head_dim-128 launches use the split form (FwdCfg SPLIT): two key
+// groups of waves share 128-key tiles, each workgroup runs a short and a
+// long query block (i and n-1-i), and the groups' partial results are merged
+// in LDS.  This evens out the work per workgroup, which otherwise grows with
+// the block index, at the cost of twice the K/V tile loads per query row.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 
-template <int D, int NW>
+// SPLIT: the waves form two key groups.  Each K/V tile then holds 128 keys;
+// wave w of group g = w / (NW/2) serves query rows 32*(w % (NW/2)) .. +31 of
+// the block against the g-th 64-key half of every tile, and the two partial
+// results of each row are merged exactly at the end (same rule as merging
+// attention over disjoint key sets).  A block has half the rows, so causal
+// launches can give every workgroup one short and one long block (see
+// launch_fwd_t).
+template <int D, int NW, bool SPLIT = false>
 struct FwdCfg {
-  static constexpr int BR = 32 * NW;  // query rows per workgroup
-  static constexpr int BC = 64;       // keys per K/V tile
+  static constexpr int KVG = SPLIT ? 2 : 1;  // key groups
+  static constexpr int RW = NW / KVG;        // waves per key group
+  static constexpr int BR = 32 * RW;         // query rows per block
+  static constexpr int BC = 64 * KVG;        // keys per K/V tile
   static constexpr int THREADS = 64 * NW;
   static constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   static constexpr int NCH = BC * CPR / THREADS;  // chunks per thread per tensor
@@ -49,15 +64,14 @@ struct FwdOccupancy {
   static constexpr int value = D == 64 ? (NW == 8 && CAUSAL ? 4 : 2) : (CAUSAL ? 2 : 1);
 };
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(FwdOccupancy<D, NW, CAUSAL>::value)))
 void fwd_kernel(FwdParams p) {
-  using Cfg = FwdCfg<D, NW>;
+  using Cfg = FwdCfg<D, NW, SPLIT>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, THREADS = Cfg::THREADS;
   constexpr int CPR = Cfg::CPR, NCH = Cfg::NCH;
   constexpr int KC = D / 16;   // 16-wide k slices of Q K^T
-  constexpr int NB = BC / 32;  // 32-key blocks per tile
   constexpr int DB = D / 32;   // 32-wide d blocks of O
   constexpr int TILE = BC * D; // halves per K (or V) tile
 
@@ -79,15 +93,25 @@ void fwd_kernel(FwdParams p) {
 
   const int BH = p.B * p.H;
   const int bh = blockIdx.x % BH;
-  const int qblk = p.num_qblocks - 1 - static_cast<int>(blockIdx.x / BH);  // heaviest first
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;    // query rows
   const int Nk = p.Nk;  // keys; causal: query i sees keys j <= i + off
   const int off = Nk - N;
+  const int g = SPLIT ? wave / Cfg::RW : 0;   // key group
+  const int rw = SPLIT ? wave % Cfg::RW : wave;
 
-  const int q0 = qblk * BR + wave * 32;  // first query row of this wave
-  const int qrow = q0 + l32;             // the query row this lane serves
+  // Query blocks of this workgroup, heaviest first.  Causal split launches
+  // pair block i with block n-1-i so that every workgroup does the same work.
+  constexpr bool PAIRED = CAUSAL && SPLIT;
+  const int slot = static_cast<int>(blockIdx.x / BH);
+  const int blk_hi = p.num_qblocks - 1 - slot;
+  const int nblk = PAIRED && slot != blk_hi ? 2 : 1;
+
+  // One query block: rows qblk*BR + 32*rw + 0..31 of this wave.
+  auto run_block = [&](const int qblk) {
+  const int q0 = qblk * BR + rw * 32;  // first query row of this wave
+  const int qrow = q0 + l32;           // the query row this lane serves
 
   // B operand of S^T = K Q^T: q[qrow][16*kc + 8*hh + 0..7].
   u32x4 qreg[KC];
@@ -105,12 +129,12 @@ void fwd_kernel(FwdParams p) {
   // Per-lane LDS offsets, fixed for the whole kernel.
   uint32_t k_off[KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) k_off[kc] = row_off<D>(lane, kc);
+  for (int kc = 0; kc < KC; ++kc) k_off[kc] = row_off<D>(lane, kc) + g * 128 * D;
   uint32_t v_off[2][DB];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) v_off[t][db] = tr_off<D, false>(lane, t, db);
+    for (int db = 0; db < DB; ++db) v_off[t][db] = tr_off<D, false>(lane, t, db) + g * 128 * D;
   // Direct global -> LDS tile loads: one global_load_lds_dwordx4 fills 1 KB
   // of a tile, lane i writing the 16-byte slot i.  Each lane therefore
   // fetches the global chunk that belongs in its slot under the tile's
@@ -177,7 +201,8 @@ void fwd_kernel(FwdParams p) {
   auto compute = [&](auto bufc, auto maskc, int kv0) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASK = decltype(maskc)::value;
-    static_assert(NB == 2, "two 32-key halves per tile");
+    // This wave's 64 keys of the tile: the key group's offset is part of
+    // k_off and v_off.
     const uint16_t* kt = BUF ? Ks1 : Ks0;
     const uint16_t* vt = BUF ? Vs1 : Vs0;
     // S^T of half nb.  C value i of lane (l32, hh): query qrow, key
@@ -279,11 +304,11 @@ void fwd_kernel(FwdParams p) {
 
   auto step = [&](auto bufc, int j) {
     constexpr int BUF = decltype(bufc)::value;
-    const int kv0 = j * BC;
+    const int kv0 = j * BC + 64 * g;  // this wave's 64 keys of the tile
     if (j + 1 < ntiles) load_tile(IntC<BUF ^ 1>{}, j + 1);
     // Causal: tiles entirely above this wave's rows carry no weight for it.
     if (!CAUSAL || kv0 <= q0 + 31 + off) {
-      const bool need_mask = (kv0 + BC > Nk) || (CAUSAL && kv0 + BC - 1 > q0 + off);
+      const bool need_mask = (kv0 + 64 > Nk) || (CAUSAL && kv0 + 63 > q0 + off);
       if (need_mask) {
         compute(bufc, IntC<1>{}, kv0);
       } else {
@@ -300,6 +325,44 @@ void fwd_kernel(FwdParams p) {
     if (j + 1 < ntiles) step(IntC<1>{}, j + 1);
   }
 
+  if constexpr (SPLIT) {
+    // Merge the two key groups' (m, l, lb, O~) of each row through LDS: the
+    // group-1 wave hands its lane values to the group-0 wave with the same
+    // rows (same lane layout).  The K/V buffers are free after the last
+    // tile barrier.  Layout [wave][value][lane], one array per d block of O~.
+    float* const xb[4] = {reinterpret_cast<float*>(Ks0), reinterpret_cast<float*>(Ks1),
+                          reinterpret_cast<float*>(Vs0), reinterpret_cast<float*>(Vs1)};
+    static_assert(DB <= 4 && Cfg::RW * 16 * 64 * 4 <= TILE * 2, "O~ exchange must fit a tile buffer");
+    float* const xs = xb[DB % 4] + (DB == 4 ? Cfg::RW * 16 * 64 : 0);
+    static_assert(Cfg::RW * 16 * 64 * 4 * (DB == 4 ? 1 : 0) + Cfg::RW * 3 * 64 * 4 <= TILE * 2,
+                  "scalar exchange must fit");
+    if (g == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xb[db][(rw * 16 + i) * 64 + lane] = oacc[db][i];
+      xs[(rw * 3 + 0) * 64 + lane] = m;
+      xs[(rw * 3 + 1) * 64 + lane] = l;
+      xs[(rw * 3 + 2) * 64 + lane] = lb;
+    }
+    __syncthreads();
+    if (g == 0) {
+      const float m1 = xs[(rw * 3 + 0) * 64 + lane];
+      const float mn = fmaxf(m, m1);
+      // m == mn also covers rows neither group has seen a key for.
+      const float a0 = m == mn ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+      const float a1 = m1 == mn ? 1.0f : __builtin_amdgcn_exp2f(m1 - mn);
+      l = l * a0 + xs[(rw * 3 + 1) * 64 + lane] * a1;
+      lb = lb * a0 + xs[(rw * 3 + 2) * 64 + lane] * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          oacc[db][i] = oacc[db][i] * a0 + xb[db][(rw * 16 + i) * 64 + lane] * a1;
+      m = mn;
+    }
+  }
+
   // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
   // O is normalised by the sum of the weights exactly as the PV product used
   // them (rounded to the input type), so each output row is a convex
@@ -309,7 +372,7 @@ void fwd_kernel(FwdParams p) {
   const float lt = sum_xor32(l);
   const float lbs = sum_xor32(lb);
   const float inv = lbs > 0.0f ? __builtin_amdgcn_rcpf(lbs) : 0.0f;
-  if (qrow < N) {
+  if (g == 0 && qrow < N) {
     uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -325,24 +388,45 @@ void fwd_kernel(FwdParams p) {
       p.lse[static_cast<int64_t>(bh) * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
     }
   }
+  };  // run_block
+
+  run_block(blk_hi);
+  if constexpr (PAIRED) {
+    if (nblk == 2) {
+      // The next block's first tile load reuses the LDS the merge just read.
+      __syncthreads();
+      run_block(slot);
+    }
+  }
 }
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool SPLIT = false>
 static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   FwdParams p = p_in;
-  p.num_qblocks = (p.N + FwdCfg<D, NW>::BR - 1) / FwdCfg<D, NW>::BR;
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_qblocks;
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
+  constexpr int BR = FwdCfg<D, NW, SPLIT>::BR;
+  p.num_qblocks = (p.N + BR - 1) / BR;
+  // Causal split launches run blocks i and n-1-i in one workgroup.
+  const int slots = CAUSAL && SPLIT ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
+  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * slots;
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPLIT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();
 }
 
-// 8 waves (256 query rows) per workgroup when that still gives at least two
-// workgroups per compute unit, else 4 waves (128 rows).  The non-causal
-// head_dim-128 kernel always uses 4 waves: at 8 it would not fit its
-// registers into the two waves per SIMD an 8-wave workgroup needs.
+// Causal head_dim 128 from N = 1024 on: the split, paired form (about 10%
+// faster than one 256-row block per workgroup at N = 8192, where that
+// launch has one workgroup per compute unit and the last blocks carry twice
+// the average work).  Otherwise 8 waves (256 query rows) per workgroup when
+// that still gives at least two workgroups per compute unit, else 4 waves
+// (128 rows).  The non-causal head_dim-128 kernel always uses 4 waves: at 8
+// it would not fit its registers into the two waves per SIMD an 8-wave
+// workgroup needs.  (The split form at head_dim 64 does not fit the 128
+// registers of its 4-waves-per-SIMD target and is not launched.)
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
+  if constexpr (CAUSAL && D == 128) {
+    if (p.N >= 1024) return launch_fwd_nw<T, D, 8, CAUSAL, true>(p, s);
+  }
   if constexpr (D == 64 || CAUSAL) {
     const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
     if (wg8 >= 512) return launch_fwd_nw<T, D, 8, CAUSAL>(p, s);

@@ -264,6 +264,29 @@ def test_unequal_lengths(Nq, Nk, D, causal, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("Nq,Nk", [(1024, 1024), (1100, 1100), (1100, 1500), (1500, 1100)])
+def test_causal_head_dim_128_long(Nq, Nk, dtype):
+    """Causal head_dim-128 launches from N_q = 1024 on run the split form:
+    two key groups per workgroup merged in LDS, query blocks i and n-1-i in
+    one workgroup.  Covers an even and an odd number of 128-row blocks, and
+    rows that see no key (N_q > N_k)."""
+    what = f"split Nq={Nq} Nk={Nk} D=128 causal {dtype}"
+    _say("case", what)
+    inp = _qk_inputs(1, Nq, Nk, 2, 128, dtype, 7700 + Nq + Nk)
+    dev = torch.device("cuda")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.to("cpu", torch.float64).numpy()
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=True)
+    _assert_forward_with_empty_rows(f64(o), f64(lse), O, LSE, what)
+    dQ, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=True)
+    for name, got, ref in (("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+        assert_grad(name, f64(got), ref, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_merge_of_key_chunks(D, dtype):
     """Key sets split into chunks, attended separately and merged through
