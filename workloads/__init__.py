@@ -18,6 +18,8 @@ from __future__ import annotations
 
 import dataclasses
 
+import math
+
 import torch
 
 DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
@@ -130,3 +132,56 @@ def sample_rows(N: int, count: int, seed: int) -> list:
         if r not in fixed:
             rows.append(r)
     return sorted(rows[:max(count, len(fixed))])
+
+
+# ------------------------------------------------------------- FP8 inputs
+#
+# FP8 attention takes E4M3 codes plus one descale factor per (batch, head)
+# for each of q, k, v (the value of code c is descale * e4m3(c)).  The
+# inputs below are quantized here with torch's own float -> float8_e4m3fn
+# conversion (round to nearest even); the codes travel as uint8 tensors.
+
+
+def quantize_e4m3_per_head(x: torch.Tensor):
+    """x [B, N, H, D] -> (codes uint8 [B, N, H, D], descale float32 [B, H]),
+    descale = max|x| / 448 over each (batch, head)."""
+    xf = x.float()
+    amax = xf.abs().amax(dim=(1, 3)).clamp_min(1e-30)
+    ds = amax / 448.0
+    y = (xf / ds[:, None, :, None]).clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), ds
+
+
+def fp8_random_inputs(B: int, Nq: int, Nk: int, H: int, D: int, seed: int) -> dict:
+    """N(0,1) q [B, Nq, H, D], k, v [B, Nk, H, D], each quantized per head."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    out = {}
+    for name, n in (("q", Nq), ("k", Nk), ("v", Nk)):
+        x = torch.randn((B, n, H, D), dtype=torch.float32, generator=gen)
+        out[name], out["descale_" + name] = quantize_e4m3_per_head(x)
+    return out
+
+
+def fp8_exact_weight_inputs(B: int, Nq: int, Nk: int, H: int, D: int, seed: int) -> dict:
+    """Inputs whose softmax weights are all powers of two.
+
+    Each q row is +-1 at one random position (zero elsewhere), every k entry
+    an integer in [-4, 4], so every raw score q.k is an integer in [-4, 4].
+    With descale_q = 1/2, descale_k = 1/4 and scale = ln(2) / (1/2 * 1/4)
+    the weight exp(scale * s) = 2^(raw score), and any weight taken relative
+    to a reference point that is itself a raw score lies in [2^-8, 2^8], all
+    exact in E4M3.  v is N(0,1) quantized per head.
+    """
+    gen = torch.Generator("cpu").manual_seed(seed)
+    pos = torch.randint(0, D, (B, Nq, H), generator=gen)
+    sign = torch.randint(0, 2, (B, Nq, H), generator=gen).float() * 2 - 1
+    qv = torch.zeros((B, Nq, H, D))
+    qv.scatter_(3, pos[..., None], sign[..., None])
+    kv = torch.randint(-4, 5, (B, Nk, H, D), generator=gen).float()
+    v = torch.randn((B, Nk, H, D), dtype=torch.float32, generator=gen)
+    out = {"q": qv.to(torch.float8_e4m3fn).view(torch.uint8),
+           "k": kv.to(torch.float8_e4m3fn).view(torch.uint8),
+           "descale_q": torch.full((B, H), 0.5), "descale_k": torch.full((B, H), 0.25)}
+    out["v"], out["descale_v"] = quantize_e4m3_per_head(v)
+    out["scale"] = math.log(2.0) / (0.5 * 0.25)
+    return out
