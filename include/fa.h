@@ -204,6 +204,35 @@ int fa_merge(const void* o_parts, const float* lse_parts, int P, void* o,
              float* lse, int B, int H, int N, int D, int dtype,
              hipStream_t stream);
 
+/*
+ * fa_fwd_fp8 -- attention forward with FP8 inputs.  FlashAttention-3 adds
+ * FP8 inputs for throughput (FlashAttention IO-awareness article at
+ * 0539edu.com, sections "H100的FP8加速能力" and "未来展望"); the pages give
+ * no format or scaling rule, and this entry point takes:
+ *   q, k, v   : device, OCP FP8 E4M3 codes (1 sign, 4 exponent bits with
+ *               bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN),
+ *               [B, Nq, H, D] and [B, Nk, H, D], d contiguous.
+ *   descale_q, descale_k, descale_v : device, fp32 [B*H] (index b*H + h),
+ *               or NULL for 1.  The value of code c is descale * e4m3(c).
+ *               Finite; any sign (a negative factor flips the scores).
+ *   o         : output, [B, Nq, H, D], out_dtype (FA_BF16 or FA_F16).
+ *   lse       : output, fp32 [B, H, Nq], natural log.
+ * Result: o = softmax(scale * Q K^T) V over the descaled values, with the
+ * softmax weights rounded to E4M3 (round to nearest even) before the
+ * product with V and the row normalised by the sum of the rounded weights;
+ * both products run on the 8-bit matrix cores with fp32 accumulation.  lse
+ * is the logsumexp of the exact scaled scores (fp32 weights).  causal and
+ * Nq != Nk: as fa_fwd_qk.  Strides (in elements, i.e. bytes for q, k, v)
+ * as fa_fwd_strides or NULL for contiguous; q, k, v strides must be
+ * multiples of 16 and their n strides below 2^24, o strides multiples of 8.
+ * Errors: as fa_fwd_qk; out_dtype other than FA_BF16 / FA_F16:
+ * FA_ERR_INVALID_ARG.  Extra device memory: none.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               const float* descale_q, const float* descale_k, const float* descale_v,
+               int B, int H, int Nq, int Nk, int D, int causal, float scale,
+               int out_dtype, const fa_fwd_strides* strides, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(int status);
 

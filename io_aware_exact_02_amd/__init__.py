@@ -5,8 +5,8 @@ this package is its thin Python binding.
 """
 
 from .attention import (FaArgError, bwd, flash_attn_func, flash_attn_qkvpacked_func, fwd,
-                        merge, workspace_bytes)
+                        fwd_fp8, merge, workspace_bytes)
 from .mha import FlashMHA
 
-__all__ = ["fwd", "bwd", "merge", "flash_attn_func", "flash_attn_qkvpacked_func",
+__all__ = ["fwd", "fwd_fp8", "bwd", "merge", "flash_attn_func", "flash_attn_qkvpacked_func",
            "workspace_bytes", "FlashMHA", "FaArgError"]

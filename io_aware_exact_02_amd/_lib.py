@@ -16,7 +16,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F16, FA_BF16 = 0, 1
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_qk", "fa_bwd", "fa_bwd_stages", "fa_bwd_qk",
+EXPORTS = ("fa_fwd", "fa_fwd_qk", "fa_fwd_fp8", "fa_bwd", "fa_bwd_stages", "fa_bwd_qk",
            "fa_bwd_workspace_bytes", "fa_bwd_qk_workspace_bytes", "fa_merge", "fa_status_str",
            "fa_version")
 STAGE_PREPROCESS, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
@@ -74,6 +74,9 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_qk.restype = i
     lib.fa_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
+                               ctypes.POINTER(FwdStrides), vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_merge.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, vp]
     lib.fa_merge.restype = i
     lib.fa_status_str.argtypes = [i]

@@ -121,6 +121,82 @@ def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
     return out, lse
 
 
+_FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _usable8(t: torch.Tensor) -> torch.Tensor:
+    """8-bit rows must start 16-byte aligned: d-stride 1, b/n/h strides that
+    are multiples of 16 bytes (n stride below 2^24) and a 16-byte aligned
+    base; copy otherwise."""
+    s = t.stride()
+    if s[3] != 1 or any(x % 16 for x in s[:3]) or s[1] >= 1 << 24 or t.data_ptr() % 16:
+        return t.contiguous()
+    return t
+
+
+def _descale(x, B: int, H: int, device) -> torch.Tensor | None:
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        return torch.full((B, H), float(x), dtype=torch.float32, device=device)
+    if x.dtype != torch.float32 or x.device != device or x.numel() != B * H:
+        raise FaArgError(f"descale factors must be float32 [B, H] = [{B}, {H}] on {device}, "
+                         f"got {x.dtype} {tuple(x.shape)} on {x.device}")
+    return x.reshape(B, H).contiguous()
+
+
+def fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal: bool = False,
+            softmax_scale=None, out_dtype=torch.bfloat16, out=None, lse=None):
+    """Forward pass with FP8 inputs.  q [B,Nq,H,D], k and v [B,Nk,H,D] hold
+    OCP E4M3 codes (torch.float8_e4m3fn, or uint8 with the same bits); the
+    optional descale factors (float32 [B, H] tensors or Python floats, None
+    for 1) give the values descale * e4m3(code).  Returns (o [B,Nq,H,D] in
+    ``out_dtype`` (bfloat16 or float16), lse [B,H,Nq] fp32)."""
+    lib = _lib.load()
+    for t in (q, k, v):
+        if t.dim() != 4:
+            raise FaArgError(f"expected [batch, seq, heads, head_dim] tensors, got {tuple(t.shape)}")
+        if t.dtype not in _FP8_DTYPES:
+            raise FaArgError(f"fwd_fp8 takes float8_e4m3fn (or uint8) codes, got {t.dtype}")
+        if t.device != q.device:
+            raise FaArgError(f"device mismatch: {t.device} vs {q.device}")
+    if k.shape != v.shape:
+        raise FaArgError(f"shape mismatch: {tuple(v.shape)} vs {tuple(k.shape)}")
+    if (q.shape[0], q.shape[2], q.shape[3]) != (k.shape[0], k.shape[2], k.shape[3]):
+        raise FaArgError(f"q {tuple(q.shape)} and k, v {tuple(k.shape)} differ in batch, heads "
+                         "or head_dim")
+    B, N, H, D = q.shape
+    Nk = k.shape[1]
+    if D not in (64, 128):
+        raise FaArgError(f"head_dim must be 64 or 128, got {D}")
+    if q.device.type != "cuda":
+        raise FaArgError(f"inputs must be on a GPU device, got {q.device}")
+    if out_dtype not in _DTYPES:
+        raise FaArgError(f"out_dtype must be float16 or bfloat16, got {out_dtype}")
+    q, k, v = (_usable8(t.view(torch.uint8)) for t in (q, k, v))
+    ds = [_descale(x, B, H, q.device) for x in (descale_q, descale_k, descale_v)]
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, N, H, D) or out.dtype != out_dtype or out.device != q.device:
+        raise FaArgError("out must be a [B, Nq, H, D] tensor of out_dtype on the inputs' device")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise FaArgError("lse must be a contiguous float32 [B, H, N] tensor")
+    out_u = _usable(out)
+    st = _lib.FwdStrides(_stride3(q), _stride3(k), _stride3(v), _stride3(out_u))
+    ptr = lambda t: None if t is None else t.data_ptr()
+    status = lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out_u.data_ptr(),
+                            lse.data_ptr(), ptr(ds[0]), ptr(ds[1]), ptr(ds[2]), B, H, N, Nk, D,
+                            int(bool(causal)), _scale(softmax_scale, D), _DTYPES[out_dtype],
+                            ctypes.byref(st), _stream(q))
+    if status != _lib.FA_OK:
+        _raise(status, "fa_fwd_fp8")
+    if out_u is not out:
+        out.copy_(out_u)
+    return out, lse
+
+
 def workspace_bytes(B: int, H: int, N: int, D: int, Nk: int | None = None) -> int:
     """Backward workspace for N query rows against Nk (default N) keys."""
     return int(_lib.load().fa_bwd_qk_workspace_bytes(B, H, N, N if Nk is None else Nk, D))

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_merge.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd8.hip", "fa_bwd.hip", "fa_merge.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled: hipcc would otherwise fuse scalar

@@ -114,6 +114,58 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               const float* descale_q, const float* descale_k, const float* descale_v, int B,
+               int H, int Nq, int Nk, int D, int causal, float scale, int out_dtype,
+               const fa_fwd_strides* strides, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, Nq, D, causal, scale, out_dtype);
+  if (st != FA_OK) return st;
+  st = check_sizes(B, H, Nk, D, causal, scale, out_dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
+  for (const void* ptr : {static_cast<const void*>(lse), static_cast<const void*>(descale_q),
+                          static_cast<const void*>(descale_k),
+                          static_cast<const void*>(descale_v)}) {
+    if ((reinterpret_cast<uintptr_t>(ptr) & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  }
+  fa::Fwd8Params p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.dsq = descale_q;
+  p.dsk = descale_k;
+  p.dsv = descale_v;
+  if (strides) {
+    p.sq = from_abi(strides->q);
+    p.sk = from_abi(strides->k);
+    p.sv = from_abi(strides->v);
+    p.so = from_abi(strides->o);
+  } else {
+    p.sq = p.so = contiguous(Nq, H, D);
+    p.sk = p.sv = contiguous(Nk, H, D);
+  }
+  if ((st = check_strides(p.so, B, Nq, H, D)) != FA_OK) return st;
+  // 8-bit rows: 16-byte aligned row starts, and one 128-row K/V tile
+  // addressed with 32-bit offsets.
+  const int rows[3] = {Nq, Nk, Nk};
+  const fa::Strides* s8[3] = {&p.sq, &p.sk, &p.sv};
+  for (int i = 0; i < 3; ++i) {
+    const fa::Strides& s = *s8[i];
+    if ((st = check_strides(s, B, rows[i], H, D)) != FA_OK) return st;
+    if (s.b % 16 || s.n % 16 || s.h % 16 || s.n >= (int64_t{1} << 24)) return FA_ERR_UNSUPPORTED;
+  }
+  p.B = B;
+  p.H = H;
+  p.N = Nq;
+  p.Nk = Nk;
+  p.c = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_fwd8(p, out_dtype, D, causal, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
            int N, int D, int causal, float scale, int dtype, const fa_fwd_strides* strides,
            hipStream_t stream) {

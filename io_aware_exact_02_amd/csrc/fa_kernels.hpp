@@ -24,6 +24,23 @@ struct FwdParams {
   int negate_q;     // 1 when scale < 0: q enters the scores negated
 };
 
+// FP8 forward: q, k, v are OCP E4M3 codes (strides in elements = bytes),
+// o is bf16 or fp16.
+struct Fwd8Params {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  uint16_t* o;
+  float* lse;  // [B, H, N] fp32
+  Strides sq, sk, sv, so;
+  const float* dsq;  // descale factors [B*H] (nullptr: 1)
+  const float* dsk;
+  const float* dsv;
+  int B, H, N, Nk;
+  int num_qblocks;
+  float c;  // scale * log2(e) (signed)
+};
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -62,5 +79,6 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStrea
 hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
                       hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_fwd8(const Fwd8Params& p, int out_dtype, int D, int causal, hipStream_t s);
 
 }  // namespace fa

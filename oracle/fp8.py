@@ -27,16 +27,26 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attention_forward, attention_probs, default_scale
+from .attention import _head_rows, attention_forward, default_scale
 
 E4M3_MAX = 448.0
 
 
+def _codes(x) -> np.ndarray:
+    """E4M3 codes as a uint8 numpy array (from numpy, or a torch uint8 or
+    float8_e4m3fn tensor)."""
+    if hasattr(x, "detach"):
+        import torch
+        t = x.detach().cpu()
+        if t.dtype != torch.uint8:
+            t = t.view(torch.uint8)
+        return t.numpy()
+    return np.asarray(x).astype(np.uint8)
+
+
 def e4m3_decode(codes) -> np.ndarray:
-    """Value of each E4M3 code (uint8 array or torch uint8 tensor), float64."""
-    if hasattr(codes, "detach"):
-        codes = codes.detach().cpu().numpy()
-    c = np.asarray(codes).astype(np.uint8).astype(np.int64)
+    """Value of each E4M3 code (uint8 array or torch tensor), float64."""
+    c = _codes(codes).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 0x7).astype(np.float64)
@@ -58,6 +68,25 @@ def attention_forward_fp8(q, k, v, descale_q, descale_k, descale_v, causal: bool
     descaled E4M3 inputs (codes [B, N, H, D], descales [B, H])."""
     return attention_forward(_descaled(q, descale_q), _descaled(k, descale_k),
                              _descaled(v, descale_v), causal=causal, scale=scale)
+
+
+def _bound_rows(Q, K, V, rows, causal, scale, offset):
+    """O, LSE and the output bound for query rows ``rows`` of one (batch,
+    head): Q [R, D] the rows' query vectors, K, V [Nk, D] descaled values."""
+    res = _head_rows(Q, K, V, rows, causal, scale, offset=offset)
+    P, O = res["P"], res["O"]                                       # [R, Nk], [R, D]
+    pmax = P.max(axis=1, keepdims=True) if P.shape[1] else np.zeros((P.shape[0], 1))
+    visible = P > 0.0
+    p = np.divide(P, pmax, out=np.zeros_like(P), where=pmax > 0)   # row max = 1
+    e = np.where(visible, np.maximum(2.0 ** -4 * p, 2.0 ** -10) + 2.0 ** -12 * p, 0.0)
+    low = np.maximum(p.sum(1) - e.sum(1), 1.0 - 2.0 ** -4 - 2.0 ** -12)  # [R]
+    num = np.empty_like(O)
+    for d in range(V.shape[1]):   # sum_j e_j |v_jd - O_id|, one d at a time
+        num[:, d] = (e * np.abs(V[None, :, d] - O[:, d:d + 1])).sum(1)
+    vmax = np.abs(V).max() if V.size else 0.0
+    bound = num / low[:, None] + 2.0 ** -8 * np.abs(O) + 1e-4 * vmax
+    bound = np.where(visible.any(1)[:, None], bound, 0.0)
+    return O, res["LSE"], bound
 
 
 def fp8_output_bound(q, k, v, descale_q, descale_k, descale_v, causal: bool = False,
@@ -84,25 +113,28 @@ def fp8_output_bound(q, k, v, descale_q, descale_k, descale_v, causal: bool = Fa
     Q = _descaled(q, descale_q)
     K = _descaled(k, descale_k)
     V = _descaled(v, descale_v)
-    if scale is None:
-        scale = default_scale(Q.shape[-1])
-    O, _ = attention_forward(Q, K, V, causal=causal, scale=scale)
-    P = attention_probs(Q, K, causal=causal, scale=scale)          # [B, H, Nq, Nk]
-    pmax = P.max(axis=-1, keepdims=True)
-    visible = P > 0.0
-    p = np.divide(P, pmax, out=np.zeros_like(P), where=pmax > 0)   # row max = 1
-    e = np.where(visible, np.maximum(2.0 ** -4 * p, 2.0 ** -10) + 2.0 ** -12 * p, 0.0)
-    low = np.maximum(p.sum(-1) - e.sum(-1), 1.0 - 2.0 ** -4 - 2.0 ** -12)  # [B, H, Nq]
-    Vh = np.transpose(V, (0, 2, 1, 3))                              # [B, H, Nk, D]
-    Oh = np.transpose(O, (0, 2, 1, 3))                              # [B, H, Nq, D]
-    # sum_j e_j |v_j - O_i| without forming [.., Nq, Nk, D]: split |a - b|
-    # by the sign of v_j - O_i per d is not linear, so loop over d.
-    num = np.empty_like(Oh)
-    for d in range(Vh.shape[-1]):
-        diff = np.abs(Vh[:, :, None, :, d] - Oh[:, :, :, None, d])  # [B, H, Nq, Nk]
-        num[..., d] = (e * diff).sum(-1)
-    vmax = np.abs(V).max(axis=(1, 3))                               # [B, H]
-    bound = num / low[..., None] + 2.0 ** -8 * np.abs(Oh) + 1e-4 * vmax[:, :, None, None]
-    empty = ~visible.any(-1)                                        # [B, H, Nq]
-    bound = np.where(empty[..., None], 0.0, bound)
-    return np.transpose(bound, (0, 2, 1, 3))
+    B, N, H, D = Q.shape
+    scale = default_scale(D) if scale is None else float(scale)
+    rows = np.arange(N)
+    out = np.zeros((B, N, H, D))
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h, :] = _bound_rows(Q[b, :, h, :], K[b, :, h, :], V[b, :, h, :], rows,
+                                          causal, scale, K.shape[1] - N)[2]
+    return out
+
+
+def fp8_rows(q, k, v, descale_q, descale_k, descale_v, b: int, h: int, rows,
+             causal: bool = False, scale: float | None = None):
+    """O [R, D], LSE [R] and the output bound [R, D] at selected query rows of
+    one (b, h), without forming the other rows."""
+    rows = np.asarray(rows)
+    ds = lambda x: np.asarray(x.detach().cpu().numpy() if hasattr(x, "detach") else x,
+                              dtype=np.float64)[b, h]
+    qc, kc, vc = _codes(q), _codes(k), _codes(v)
+    Q = e4m3_decode(qc[b, rows, h, :]) * ds(descale_q)
+    K = e4m3_decode(kc[b, :, h, :]) * ds(descale_k)
+    V = e4m3_decode(vc[b, :, h, :]) * ds(descale_v)
+    scale = default_scale(K.shape[1]) if scale is None else float(scale)
+    O, LSE, bound = _bound_rows(Q, K, V, rows, causal, scale, kc.shape[1] - qc.shape[1])
+    return {"O": O, "LSE": LSE, "bound": bound}

@@ -223,3 +223,43 @@ def test_python_binding_checks_unequal_lengths_without_gpu():
     with pytest.raises(fa.FaArgError, match="lse_parts"):
         fa.merge(torch.zeros(2, 1, 16, 2, 64, dtype=torch.bfloat16),
                  torch.zeros(2, 1, 2, 17, dtype=torch.float32))
+
+
+def test_fp8_rejects_before_launch():
+    lib = _lib.load()
+
+    def f8(q=P, k=P, v=P, o=P, lse=P, dq=None, dk=None, dv=None, B=1, H=2, Nq=64, Nk=64,
+           D=64, causal=0, scale=0.125, out=_lib.FA_BF16, strides=None):
+        st = None if strides is None else ctypes.byref(strides)
+        return lib.fa_fwd_fp8(q, k, v, o, lse, dq, dk, dv, B, H, Nq, Nk, D, causal, scale, out,
+                              st, None)
+
+    assert f8(q=None) == _lib.FA_ERR_INVALID_ARG
+    assert f8(lse=None) == _lib.FA_ERR_INVALID_ARG
+    assert f8(Nk=0) == _lib.FA_ERR_INVALID_ARG
+    assert f8(out=7) == _lib.FA_ERR_INVALID_ARG
+    assert f8(causal=2) == _lib.FA_ERR_INVALID_ARG
+    assert f8(scale=float("nan")) == _lib.FA_ERR_INVALID_ARG
+    assert f8(D=96) == _lib.FA_ERR_UNSUPPORTED
+    assert f8(v=P + 8) == _lib.FA_ERR_UNSUPPORTED
+    assert f8(dk=P + 2) == _lib.FA_ERR_UNSUPPORTED
+    s = _lib.Stride3(64 * 2 * 64, 2 * 64, 64)
+    ok = _lib.FwdStrides(s, s, s, s)
+    bad8 = _lib.FwdStrides(_lib.Stride3(64 * 2 * 64, 2 * 64 + 8, 64), s, s, s)  # 8, not 16
+    huge = _lib.FwdStrides(s, _lib.Stride3(1 << 30, 1 << 24, 64), s, s)
+    assert f8(strides=bad8) == _lib.FA_ERR_UNSUPPORTED
+    assert f8(strides=huge) == _lib.FA_ERR_UNSUPPORTED
+    del ok
+
+
+def test_fp8_binding_checks_without_gpu():
+    q = torch.zeros(1, 16, 2, 64, dtype=torch.uint8)
+    with pytest.raises(fa.FaArgError, match="float8"):
+        fa.fwd_fp8(q.to(torch.bfloat16), q, q)
+    with pytest.raises(fa.FaArgError, match="head_dim"):
+        fa.fwd_fp8(*(torch.zeros(1, 16, 2, 32, dtype=torch.uint8),) * 3)
+    with pytest.raises(fa.FaArgError, match="GPU"):
+        fa.fwd_fp8(q, q.view(torch.float8_e4m3fn), q)
+    with pytest.raises(fa.FaArgError, match="differ"):
+        fa.fwd_fp8(q, torch.zeros(1, 16, 3, 64, dtype=torch.uint8),
+                   torch.zeros(1, 16, 3, 64, dtype=torch.uint8))

@@ -132,6 +132,22 @@ def pin_bound_subnormal_floor():
     assert worst > 0.5, worst
 
 
+def pin_rows_match_full():
+    """The row-sampled bound and forward equal the full ones at those rows."""
+    for causal, (nq, nk) in ((False, (30, 30)), (True, (30, 30)), (True, (40, 25))):
+        d = fp8_random_inputs(2, nq, nk, 2, 64, 41)
+        args = (d["q"], d["k"], d["v"], d["descale_q"], d["descale_k"], d["descale_v"])
+        O, LSE = o8.attention_forward_fp8(*args, causal=causal)
+        E = o8.fp8_output_bound(*args, causal=causal)
+        rows = [0, 7, nq - 1]
+        r = o8.fp8_rows(*args, 1, 1, rows, causal=causal)
+        assert np.allclose(r["O"], O[1, rows, 1], rtol=0, atol=1e-14)
+        assert np.array_equal(np.isneginf(r["LSE"]), np.isneginf(LSE[1, 1, rows]))
+        fin = np.isfinite(r["LSE"])
+        assert np.allclose(r["LSE"][fin], LSE[1, 1, rows][fin], rtol=0, atol=1e-14)
+        assert np.allclose(r["bound"], E[1, rows, 1], rtol=0, atol=1e-14)
+
+
 def pin_exact_weight_inputs():
     """The exact-weight recipe: every weight a power of two in [2^-8, 2^8]."""
     d = fp8_exact_weight_inputs(1, 30, 50, 2, 64, 31)
@@ -146,7 +162,8 @@ def pin_exact_weight_inputs():
 
 
 ALL_PINS = [pin_decode_table, pin_forward_is_attention_of_values, pin_bound_random_rows,
-            pin_bound_rounding_tie, pin_bound_subnormal_floor, pin_exact_weight_inputs]
+            pin_bound_rounding_tie, pin_bound_subnormal_floor, pin_rows_match_full,
+            pin_exact_weight_inputs]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -164,14 +181,14 @@ MUTANTS = {
                             "np.maximum(2.0 ** -5 * p, 2.0 ** -10)"),
     "bound_no_subnormal_floor": ("np.maximum(2.0 ** -4 * p, 2.0 ** -10)",
                                  "np.maximum(2.0 ** -4 * p, 0.0)"),
-    "bound_unrounded_denominator": ("p.sum(-1) - e.sum(-1)", "p.sum(-1) + e.sum(-1)"),
+    "bound_unrounded_denominator": ("p.sum(1) - e.sum(1)", "p.sum(1) + e.sum(1)"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutants_are_caught(name, monkeypatch):
     old, new = MUTANTS[name]
-    fn = o8.e4m3_decode if name.startswith("decode") else o8.fp8_output_bound
+    fn = o8.e4m3_decode if name.startswith("decode") else o8._bound_rows
     src = inspect.getsource(fn)
     assert src.count(old) == 1, f"mutation site for {name} not found"
     ns = dict(vars(o8))

@@ -152,13 +152,19 @@ def quantize_e4m3_per_head(x: torch.Tensor):
     return y.to(torch.float8_e4m3fn).view(torch.uint8), ds
 
 
-def fp8_random_inputs(B: int, Nq: int, Nk: int, H: int, D: int, seed: int) -> dict:
-    """N(0,1) q [B, Nq, H, D], k, v [B, Nk, H, D], each quantized per head."""
+def fp8_random_inputs(B: int, Nq: int, Nk: int, H: int, D: int, seed: int,
+                      per_head_scale: bool = True) -> dict:
+    """N(0,1) q [B, Nq, H, D], k, v [B, Nk, H, D], each quantized per head
+    (or, with per_head_scale=False, cast directly: descale factors of 1)."""
     gen = torch.Generator("cpu").manual_seed(seed)
     out = {}
     for name, n in (("q", Nq), ("k", Nk), ("v", Nk)):
         x = torch.randn((B, n, H, D), dtype=torch.float32, generator=gen)
-        out[name], out["descale_" + name] = quantize_e4m3_per_head(x)
+        if per_head_scale:
+            out[name], out["descale_" + name] = quantize_e4m3_per_head(x)
+        else:
+            out[name] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+            out["descale_" + name] = torch.ones((B, H))
     return out
 
 
