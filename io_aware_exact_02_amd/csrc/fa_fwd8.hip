@@ -69,8 +69,17 @@ struct Fwd8Cfg {
   static_assert(NCH * THREADS == BC * CPR, "tile load must divide evenly");
 };
 
+// Waves per SIMD the register allocation targets: at head_dim 64 the kernel
+// is bound by its softmax VALU work and needs several waves to overlap it
+// with the matrix cores.
+template <int D>
+struct Fwd8Occupancy {
+  static constexpr int value = D == 64 ? 3 : 2;
+};
+
 template <typename T, int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void fwd8_kernel(Fwd8Params p) {
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(Fwd8Params p) {
   using Cfg = Fwd8Cfg<D, NW>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, CPR = Cfg::CPR, NCH = Cfg::NCH;
   constexpr int KC = D / 64;   // 64-wide k slices of Q K^T
@@ -231,22 +240,23 @@ __global__ __launch_bounds__(64 * NW) void fwd8_kernel(Fwd8Params p) {
     }
     // Weights against the reference point m (moved, with a rescale, only
     // when this lane's sum over the unit would exceed 2^8 or on the first
-    // keys), rounded to E4M3 into the B operand: byte j = 16*nb + i holds
-    // the weight of key 32*nb + c_item(i, hh).
-    float pw[2][16];
+    // keys), rounded to E4M3 straight into the B operand: byte j = 16*nb + i
+    // (dword j / 4) holds the weight of key 32*nb + c_item(i, hh).
+    u32x8 pb;
     float lt;
     auto weights = [&]() {
       const float negm = -fmaxf(m, -3.0e38f);
       float a = 0.0f, c = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int w = 0; w < 8; ++w) {
+        float x[4];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          pw[nb][i] = __builtin_amdgcn_exp2f(fmaf(s[nb][i], c_scale, negm));
-          pw[nb][i + 1] = __builtin_amdgcn_exp2f(fmaf(s[nb][i + 1], c_scale, negm));
-          a += pw[nb][i];
-          c += pw[nb][i + 1];
-        }
+        for (int e = 0; e < 4; ++e)
+          x[e] = __builtin_amdgcn_exp2f(fmaf(s[w >> 2][4 * (w & 3) + e], c_scale, negm));
+        a += x[0] + x[2];
+        c += x[1] + x[3];
+        pb[w] = pack4_e4m3(x[0], x[1], x[2], x[3]);
+      }
       lt = a + c;
     };
     weights();
@@ -267,12 +277,6 @@ __global__ __launch_bounds__(64 * NW) void fwd8_kernel(Fwd8Params p) {
       weights();
     }
     l += lt;
-    u32x8 pb;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const float* x = &pw[w >> 2][4 * (w & 3)];
-      pb[w] = pack4_e4m3(x[0], x[1], x[2], x[3]);
-    }
     // O^T += V^T P^T per d block, and the sum of the rounded weights.
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
