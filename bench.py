@@ -26,6 +26,8 @@ Prints ONE JSON line.  Besides the headline value it carries
   pages_sweep  : the pages' own forward speed comparison (standard fp16
                  attention vs the fused kernel, B=2 H=8 D=64 fp16 at
                  N = 2048/4096/8192, causal at 4096), untimed by the step;
+  fp8_forward  : the FP8 (E4M3) forward at the sweep's shapes against the
+                 dense fp8 peak and the 16-bit forward, untimed by the step;
   mha_layer    : forward + backward of the whole multi-head attention layer
                  (QKV projection, attention, output projection) with the
                  fused kernels against the same layer with standard fp16
@@ -221,6 +223,47 @@ def pages_sweep(torch, fa):
             "causal_vs_noncausal_fused_speedup_N4096": round(fused_ms["s4096"] / fused_ms["s4096c"], 2)}
 
 
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA: twice the 16-bit rate
+
+
+def fp8_forward(torch, fa, per_config):
+    """The FP8 forward (E4M3 q, k, v with per-head descale factors, bf16
+    output) at the shapes of the 16-bit sweep: time, TFLOP/s against the
+    dense fp8 peak, and the speedup over the 16-bit forward measured in the
+    same run.  Inputs: N(0,1) quantized per (batch, head), resident in HBM."""
+    from workloads import WORKLOADS, fp8_random_inputs
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream(dev)
+    rows = {}
+    for name, cfg in per_config.items():
+        w = WORKLOADS[name]
+        d = fp8_random_inputs(w.B, w.N, w.N, w.H, w.D, 9100 + w.N)
+        q, k, v = (d[n].to(dev) for n in ("q", "k", "v"))
+        ds = [d["descale_" + n].to(dev) for n in ("q", "k", "v")]
+        o = torch.empty((w.B, w.N, w.H, w.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        run = lambda: fa.fwd_fp8(q, k, v, *ds, causal=w.causal, out=o, lse=lse)
+        for _ in range(3):
+            run()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(10):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 10
+        f = 4.0 * w.B * w.H * w.N * w.N * w.D / (2 if w.causal else 1)
+        rows[name] = {"shape": f"B={w.B} H={w.H} N={w.N} D={w.D} e4m3 "
+                               f"{'causal' if w.causal else 'non-causal'}",
+                      "fwd_ms": round(ms, 4), "fwd_tflops": round(f / ms / 1e9, 2),
+                      "pct_fp8_peak": round(100 * f / ms / 1e9 / PEAK_FP8_TFLOPS, 2),
+                      "speedup_vs_16bit_fwd": round(cfg["fwd_ms"] / ms, 2)}
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return rows
+
+
 def mha_layer(torch, fa):
     """Training step of the multi-head attention layer (forward and backward
     of FlashMHA, random-init fp16 weights) at B=2, N=2048, embed 768, 12
@@ -286,6 +329,7 @@ def main(argv=None):
     ap.add_argument("--no-pages-sweep", action="store_true",
                     help="skip the standard-vs-fused forward sweep of the pages (N=2048..8192)")
     ap.add_argument("--no-mha", action="store_true", help="skip the attention-layer measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise kernel that reads and "
                          "writes this many MiB (calibrates HBM byte counters)")
@@ -412,6 +456,10 @@ def main(argv=None):
     if not args.no_pages_sweep:
         sweep = pages_sweep(torch, fa)
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = fp8_forward(torch, fa, per_config)
+
     layer = None
     if not args.no_mha:
         layer = mha_layer(torch, fa)
@@ -445,6 +493,7 @@ def main(argv=None):
         "memory_c3": memory,
         "pages_sweep": sweep,
         "mha_layer": layer,
+        "fp8_forward": fp8,
     }
     print(json.dumps(out), flush=True)
     return 0

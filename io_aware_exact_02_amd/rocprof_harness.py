@@ -8,8 +8,9 @@ Four rocprofv3 runs of ``bench.py`` (each its own process; counters never
 share a run with tracing):
 
 1. ``--kernel-trace --stats``: per-kernel dispatch count and durations;
-2. ``--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16``: executed
-   matrix-core FLOPs (512 FLOPs per MOPS unit), per dispatch;
+2. ``--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16
+   SQ_INSTS_VALU_MFMA_MOPS_F8``: executed matrix-core FLOPs (512 FLOPs per
+   MOPS unit), per dispatch;
 3. ``--pmc FETCH_SIZE`` and 4. ``--pmc WRITE_SIZE``: bytes between L2 and
    memory (KiB per dispatch), each calibrated against one elementwise kernel
    of known size (one read and one write of ``--calib-mib`` MiB) run in the
@@ -17,7 +18,8 @@ share a run with tracing):
 
 It prints the summary and, with ``--summary-dir``, writes
 ``kernels_<workloads>.txt`` (durations, executed MFMA TFLOP/s against the
-2516.6 TFLOP/s dense bf16/fp16 peak, L2-to-memory GB/s) and, when c5 is
+dense peak of the kernel's type -- 2516.6 TFLOP/s bf16/fp16, 5033.2 TFLOP/s
+fp8 -- and L2-to-memory GB/s) and, when c5 is
 profiled, ``traffic_bwd_dkdv_c5.json`` -- the calibrated bytes per launch of
 the dK/dV kernel together with a hash of its sources, which ``bench.py``
 reports as the roofline's ``traffic`` while the sources are unchanged.
@@ -40,6 +42,7 @@ import time
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 BENCH = os.path.join(ROOT, "bench.py")
 PEAK_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_02_amd", "csrc", f)
                   for f in ("fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp")]
 
@@ -126,7 +129,8 @@ def main(argv=None):
     stats = read_csv(os.path.join(a.raw, "trace", "**", "*kernel_stats.csv"))
     trace = read_csv(os.path.join(a.raw, "trace", "**", "*kernel_trace.csv"))
     passes = {
-        "mfma": ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16"],
+        "mfma": ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F8"],
         "fetch": ["FETCH_SIZE"],
         "write": ["WRITE_SIZE"],
     }
@@ -159,11 +163,9 @@ def main(argv=None):
              "command: python -m io_aware_exact_02_amd.rocprof_harness --raw <dir> "
              f"--workloads {a.workloads} --steps {a.steps} --calib-mib {a.calib_mib}",
              "  runs: rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py "
-             f"--steps {a.steps} --warmup 2 --cpu-seconds 0 --no-memory --no-pages-sweep --no-mha "
-             f"--workloads {a.workloads} "
-             f"--copy-calibration-mib {a.calib_mib}",
-             "        and the same command under rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
-             "SQ_INSTS_VALU_MFMA_MOPS_F16 / --pmc FETCH_SIZE / --pmc WRITE_SIZE",
+             + " ".join(bench[2:]),
+             "        and the same command under rocprofv3 --pmc "
+             + " ".join(passes["mfma"]) + " / --pmc FETCH_SIZE / --pmc WRITE_SIZE",
              f"calibration: elementwise kernel of {a.calib_mib} MiB read + write; counter scale "
              f"FETCH x{f_scale:.4f}, WRITE x{w_scale:.4f}" if f_scale else "calibration: none",
              "",
@@ -184,8 +186,9 @@ def main(argv=None):
         rd_b = (sum(fe) / len(fe)) * 1024 * (f_scale or 1.0) if fe else None
         wr_b = (sum(wr) / len(wr)) * 1024 * (w_scale or 1.0) if wr else None
         tf = flops / avg / 1e12 if avg > 0 else 0.0
+        peak = PEAK_FP8_TFLOPS if "fwd8" in k else PEAK_TFLOPS
         lines.append(f"{k[:64]:64s} {len(d):5d} {avg * 1e6:9.1f} {min(d) * 1e6:9.1f} "
-                     f"{tf:9.1f} {100 * tf / PEAK_TFLOPS:6.1f} "
+                     f"{tf:9.1f} {100 * tf / peak:6.1f} "
                      f"{(rd_b / avg / 1e9) if rd_b else 0:8.1f} {(wr_b / avg / 1e9) if wr_b else 0:8.1f}")
         # The dominant kernel: the bf16 head_dim-64 causal dK/dV kernel (only
         # c5 launches it), the longest-running entry of that name.
