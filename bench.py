@@ -26,6 +26,8 @@ Prints ONE JSON line.  Besides the headline value it carries
   pages_sweep  : the pages' own forward speed comparison (standard fp16
                  attention vs the fused kernel, B=2 H=8 D=64 fp16 at
                  N = 2048/4096/8192, causal at 4096), untimed by the step;
+  head_shard_c5_of_8 : one GPU's share of c5 split by heads over 8 GPUs
+                 (B=1 H=2 N=16384 D=64 causal), forward + backward;
   fp8_forward  : the FP8 (E4M3) forward at the sweep's shapes against the
                  dense fp8 peak and the 16-bit forward, untimed by the step;
   mha_layer    : forward + backward of the whole multi-head attention layer
@@ -96,6 +98,17 @@ def cpu_threads() -> int:
     return len(os.sched_getaffinity(0))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s: float):
     """The fp64 oracle (as it stands) on whole heads of c5, the workload that
     dominates the sweep, until the budget is used (at least one head);
@@ -119,7 +132,8 @@ def cpu_baseline(budget_s: float):
     return {"value": round(done * per_head / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": cpu_threads(), "kind": "oracle",
             "sample": f"fp64 numpy oracle, fwd+bwd of {done} of the {w.B * w.H} heads of c5 "
-                      f"({w.describe()}), {dt:.1f} s"}
+                      f"({w.describe()}), {dt:.1f} s; host {cpu_model()}, "
+                      f"{len(os.sched_getaffinity(0))} cores in affinity"}
 
 
 def unfused_memory_c3(torch, fa, w, inp):
@@ -264,6 +278,42 @@ def fp8_forward(torch, fa, per_config):
     return rows
 
 
+def head_shard(torch, fa):
+    """One GPU's share of c5 when its 16 heads are split over 8 GPUs (no
+    exchange needed): B=1 H=2 N=16384 D=64 bf16 causal, forward + backward
+    through the C ABI, 10 timed steps after 3 warm-ups.  256 workgroups in
+    the backward and 128 in the forward: one GPU's view of head sharding."""
+    from workloads import Workload, make_inputs
+    dev = torch.device("cuda")
+    w = Workload("c5/8", 1, 2, 16384, 64, "bf16", True, "bnhd", 1005)
+    inp = make_inputs(w)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.workspace_bytes(1, 2, w.N, 64), dtype=torch.uint8, device=dev)
+
+    def run():
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        fa.bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(3):
+        run()
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(10):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    fwd_f, bwd_f = conv_flops(w)
+    return {"shape": w.describe(), "ms_per_step": round(ms, 4),
+            "tflops": round((fwd_f + bwd_f) / ms / 1e9, 2),
+            "pct_peak": round(100 * (fwd_f + bwd_f) / ms / 1e9 / PEAK_MFMA_TFLOPS, 2)}
+
+
 def mha_layer(torch, fa):
     """Training step of the multi-head attention layer (forward and backward
     of FlashMHA, random-init fp16 weights) at B=2, N=2048, embed 768, 12
@@ -330,6 +380,8 @@ def main(argv=None):
                     help="skip the standard-vs-fused forward sweep of the pages (N=2048..8192)")
     ap.add_argument("--no-mha", action="store_true", help="skip the attention-layer measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the one-GPU share of c5 under 8-way head sharding")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise kernel that reads and "
                          "writes this many MiB (calibrates HBM byte counters)")
@@ -456,6 +508,10 @@ def main(argv=None):
     if not args.no_pages_sweep:
         sweep = pages_sweep(torch, fa)
 
+    shard = None
+    if not args.no_shard:
+        shard = head_shard(torch, fa)
+
     fp8 = None
     if not args.no_fp8:
         fp8 = fp8_forward(torch, fa, per_config)
@@ -494,6 +550,13 @@ def main(argv=None):
         "pages_sweep": sweep,
         "mha_layer": layer,
         "fp8_forward": fp8,
+        "head_shard_c5_of_8": shard,
+        "device": {"name": torch.cuda.get_device_properties(0).name,
+                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+                   "derived_peak_tflops": round(
+                       torch.cuda.get_device_properties(0).multi_processor_count
+                       * 2.4e9 * 4096 / 1e12, 1),
+                   "clock_for_peak_ghz": 2.4},
     }
     print(json.dumps(out), flush=True)
     return 0
