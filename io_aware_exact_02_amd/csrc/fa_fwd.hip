@@ -110,284 +110,286 @@ void fwd_kernel(FwdParams p) {
 
   // One query block: rows qblk*BR + 32*rw + 0..31 of this wave.
   auto run_block = [&](const int qblk) {
-  const int q0 = qblk * BR + rw * 32;  // first query row of this wave
-  const int qrow = q0 + l32;           // the query row this lane serves
+    const int q0 = qblk * BR + rw * 32;  // first query row of this wave
+    const int qrow = q0 + l32;           // the query row this lane serves
 
-  // B operand of S^T = K Q^T: q[qrow][16*kc + 8*hh + 0..7].
-  u32x4 qreg[KC];
-  {
-    const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h + static_cast<int64_t>(qrow) * p.sq.n + 8 * hh;
-    const uint32_t sign = p.negate_q ? 0x80008000u : 0u;
+    // B operand of S^T = K Q^T: q[qrow][16*kc + 8*hh + 0..7].
+    u32x4 qreg[KC];
+    {
+      const uint16_t* qp =
+          p.q + b * p.sq.b + h * p.sq.h + static_cast<int64_t>(qrow) * p.sq.n + 8 * hh;
+      const uint32_t sign = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow < N) v = ldg16(qp + 16 * kc);
-      qreg[kc] = v ^ sign;
+      for (int kc = 0; kc < KC; ++kc) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qrow < N) v = ldg16(qp + 16 * kc);
+        qreg[kc] = v ^ sign;
+      }
     }
-  }
 
-  // Per-lane LDS offsets, fixed for the whole kernel.
-  uint32_t k_off[KC];
+    // Per-lane LDS offsets (this wave's key group included).
+    uint32_t k_off[KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) k_off[kc] = row_off<D>(lane, kc) + g * 128 * D;
-  uint32_t v_off[2][DB];
+    for (int kc = 0; kc < KC; ++kc) k_off[kc] = row_off<D>(lane, kc) + g * 128 * D;
+    uint32_t v_off[2][DB];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) v_off[t][db] = tr_off<D, false>(lane, t, db) + g * 128 * D;
-  // Direct global -> LDS tile loads: one global_load_lds_dwordx4 fills 1 KB
-  // of a tile, lane i writing the 16-byte slot i.  Each lane therefore
-  // fetches the global chunk that belongs in its slot under the tile's
-  // layout (swizzled chunks; sigma_row for K).  Offsets in elements, within
-  // a tile of BC rows.
-  uint32_t gk_off[NCH], gv_off[NCH];
-#pragma unroll
-  for (int it = 0; it < NCH; ++it) {
-    const int slot = (wave + NW * it) * 64 + lane;
-    const int pr = slot / CPR;                            // stored row
-    const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;      // logical column
-    gk_off[it] = static_cast<uint32_t>(sigma_row(pr) * p.sk.n + col);
-    gv_off[it] = static_cast<uint32_t>(pr * p.sv.n + col);
-  }
-  const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
-  const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
-  float m = -INFINITY;  // reference point (exp2 units) of this row's weights
-  float l = 0.0f;       // sum of the fp32 weights exp2(t - m), this lane's keys
-  float lb = 0.0f;      // sum of the same weights as rounded for the PV product
-  const float c_scale = p.c;
-
-  const int qlast = min(qblk * BR + BR, N) - 1;
-  // Causal: up to the last key the workgroup's last row sees (at least one
-  // tile, so that rows seeing no key still go through the masked path).
-  const int ntiles = CAUSAL ? (max(min(qlast + off, Nk - 1), 0) / BC + 1) : ((Nk + BC - 1) / BC);
-
-  // Issue the loads of tile j into buffer BUF.  Rows past N (last tile only)
-  // are clamped to row N-1: those keys are masked, so their finite values
-  // never reach the result.
-  auto load_tile = [&](auto bufc, int j) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int kv0 = j * BC;
-    const uint16_t* kt = kbase + static_cast<int64_t>(kv0) * p.sk.n;
-    const uint16_t* vt = vbase + static_cast<int64_t>(kv0) * p.sv.n;
-    const bool tail = kv0 + BC > Nk;
+      for (int db = 0; db < DB; ++db) v_off[t][db] = tr_off<D, false>(lane, t, db) + g * 128 * D;
+    // Direct global -> LDS tile loads: one global_load_lds_dwordx4 fills 1 KB
+    // of a tile, lane i writing the 16-byte slot i.  Each lane therefore
+    // fetches the global chunk that belongs in its slot under the tile's
+    // layout (swizzled chunks; sigma_row for K).  Offsets in elements, within
+    // a tile of BC rows.
+    uint32_t gk_off[NCH], gv_off[NCH];
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      uint32_t ko = gk_off[it], vo = gv_off[it];
-      if (tail) {
-        const int last = Nk - 1 - kv0;
-        const int slot = (wave + NW * it) * 64 + lane;
-        const int pr = slot / CPR;
-        const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;
-        ko = static_cast<uint32_t>(min(sigma_row(pr), last) * p.sk.n + col);
-        vo = static_cast<uint32_t>(min(pr, last) * p.sv.n + col);
-      }
-      lds_dma16(kt + ko, (BUF ? Ks1 : Ks0) + (wave + NW * it) * 512);
-      lds_dma16(vt + vo, (BUF ? Vs1 : Vs0) + (wave + NW * it) * 512);
+      const int slot = (wave + NW * it) * 64 + lane;
+      const int pr = slot / CPR;                            // stored row
+      const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;      // logical column
+      gk_off[it] = static_cast<uint32_t>(sigma_row(pr) * p.sk.n + col);
+      gv_off[it] = static_cast<uint32_t>(pr * p.sv.n + col);
     }
-  };
-  // Wait for this wave's tile loads, then for every wave's.
-  auto tile_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-  };
+    const uint16_t* kbase = p.k + b * p.sk.b + h * p.sk.h;
+    const uint16_t* vbase = p.v + b * p.sv.b + h * p.sv.h;
 
-  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T, taken as two
-  // 32-key halves so that the softmax of the first half can overlap the
-  // second half's S product and the second softmax the first PV product.
-  auto compute = [&](auto bufc, auto maskc, int kv0) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr bool MASK = decltype(maskc)::value;
-    // This wave's 64 keys of the tile: the key group's offset is part of
-    // k_off and v_off.
-    const uint16_t* kt = BUF ? Ks1 : Ks0;
-    const uint16_t* vt = BUF ? Vs1 : Vs0;
-    // S^T of half nb.  C value i of lane (l32, hh): query qrow, key
-    // kv0 + 32*nb + c_item(i, hh).
-    auto s_half = [&](int nb) {
-      f32x16 acc = (f32x16){};
+    f32x16 oacc[DB];
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        acc = mfma32x32x16<T>(lds_ld16(kt + 32 * nb * D, k_off[kc]), qreg[kc], acc);
-      return acc;
-    };
-    auto mask_half = [&](f32x16& acc, int nb) {
-      if constexpr (MASK) {
+    for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
+    float m = -INFINITY;  // reference point (exp2 units) of this row's weights
+    float l = 0.0f;       // sum of the fp32 weights exp2(t - m), this lane's keys
+    float lb = 0.0f;      // sum of the same weights as rounded for the PV product
+    const float c_scale = p.c;
+
+    const int qlast = min(qblk * BR + BR, N) - 1;
+    // Causal: up to the last key the workgroup's last row sees (at least one
+    // tile, so that rows seeing no key still go through the masked path).
+    const int ntiles = CAUSAL ? (max(min(qlast + off, Nk - 1), 0) / BC + 1) : ((Nk + BC - 1) / BC);
+
+    // Issue the loads of tile j into buffer BUF.  Rows past N (last tile only)
+    // are clamped to row N-1: those keys are masked, so their finite values
+    // never reach the result.
+    auto load_tile = [&](auto bufc, int j) {
+      constexpr int BUF = decltype(bufc)::value;
+      const int kv0 = j * BC;
+      const uint16_t* kt = kbase + static_cast<int64_t>(kv0) * p.sk.n;
+      const uint16_t* vt = vbase + static_cast<int64_t>(kv0) * p.sv.n;
+      const bool tail = kv0 + BC > Nk;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + 32 * nb + c_item(i, hh);
-          if (key >= Nk || (CAUSAL && key > qrow + off)) acc[i] = -INFINITY;
+      for (int it = 0; it < NCH; ++it) {
+        uint32_t ko = gk_off[it], vo = gv_off[it];
+        if (tail) {
+          const int last = Nk - 1 - kv0;
+          const int slot = (wave + NW * it) * 64 + lane;
+          const int pr = slot / CPR;
+          const int col = ((slot % CPR) ^ swz<D>(pr)) * 8;
+          ko = static_cast<uint32_t>(min(sigma_row(pr), last) * p.sk.n + col);
+          vo = static_cast<uint32_t>(min(pr, last) * p.sv.n + col);
         }
+        lds_dma16(kt + ko, (BUF ? Ks1 : Ks0) + (wave + NW * it) * 512);
+        lds_dma16(vt + vo, (BUF ? Vs1 : Vs0) + (wave + NW * it) * 512);
       }
     };
-    // Weights of one half, p = exp2(c*s - m), as MFMA operands.  They are
-    // computed against the current reference point m; m only moves when that
-    // makes this lane's sum over the half exceed 2^8 (or on the first tile,
-    // where m is -inf and the sum is not finite): then m becomes the running
-    // row max, the accumulators are rescaled and the weights recomputed.  So
-    // every weight stays below 2^8 and the row max is only taken when m
-    // moves.  O = sum p v / sum p and LSE = m + log2(sum p) hold for any m:
-    // this changes no result, only how often the accumulators are rescaled.
-    auto soft_half = [&](const f32x16& acc, u32x4 (&pbh)[2]) {
-      float lt, lbt;
-      auto weights = [&]() {
-        // m = -inf (no key seen yet): a huge finite shift instead, so that
-        // visible keys overflow the sum (and move m) while masked ones give 0.
-        const float negm = -fmaxf(m, -3.0e38f);
-        float pv[16];
+    // Wait for this wave's tile loads, then for every wave's.
+    auto tile_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    };
+
+    // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T, taken as two
+    // 32-key halves so that the softmax of the first half can overlap the
+    // second half's S product and the second softmax the first PV product.
+    auto compute = [&](auto bufc, auto maskc, int kv0) {
+      constexpr int BUF = decltype(bufc)::value;
+      constexpr bool MASK = decltype(maskc)::value;
+      // This wave's 64 keys of the tile: the key group's offset is part of
+      // k_off and v_off.
+      const uint16_t* kt = BUF ? Ks1 : Ks0;
+      const uint16_t* vt = BUF ? Vs1 : Vs0;
+      // S^T of half nb.  C value i of lane (l32, hh): query qrow, key
+      // kv0 + 32*nb + c_item(i, hh).
+      auto s_half = [&](int nb) {
+        f32x16 acc = (f32x16){};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c_scale, negm));
-        float s0 = 0.0f, s1 = 0.0f;
+        for (int kc = 0; kc < KC; ++kc)
+          acc = mfma32x32x16<T>(lds_ld16(kt + 32 * nb * D, k_off[kc]), qreg[kc], acc);
+        return acc;
+      };
+      auto mask_half = [&](f32x16& acc, int nb) {
+        if constexpr (MASK) {
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          s0 += pv[i];
-          s1 += pv[i + 1];
-        }
-        lt = s0 + s1;
-        pbh[0] = pack8<T>(pv);
-        pbh[1] = pack8<T>(pv + 8);
-        lbt = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          lbt = sum2_acc<T>(pbh[0][w], lbt);
-          lbt = sum2_acc<T>(pbh[1][w], lbt);
+          for (int i = 0; i < 16; ++i) {
+            const int key = kv0 + 32 * nb + c_item(i, hh);
+            if (key >= Nk || (CAUSAL && key > qrow + off)) acc[i] = -INFINITY;
+          }
         }
       };
-      weights();
-      if (__any(!(lt <= 256.0f))) {
-        // Keeps this rarely taken block a real branch: without it the
-        // compiler if-converts it and rescales the accumulator every time.
-        asm volatile("" ::: "memory");
-        float mx0 = acc[0], mx1 = acc[1];
+      // Weights of one half, p = exp2(c*s - m), as MFMA operands.  They are
+      // computed against the current reference point m; m only moves when that
+      // makes this lane's sum over the half exceed 2^8 (or on the first tile,
+      // where m is -inf and the sum is not finite): then m becomes the running
+      // row max, the accumulators are rescaled and the weights recomputed.  So
+      // every weight stays below 2^8 and the row max is only taken when m
+      // moves.  O = sum p v / sum p and LSE = m + log2(sum p) hold for any m:
+      // this changes no result, only how often the accumulators are rescaled.
+      auto soft_half = [&](const f32x16& acc, u32x4 (&pbh)[2]) {
+        float lt, lbt;
+        auto weights = [&]() {
+          // m = -inf (no key seen yet): a huge finite shift instead, so that
+          // visible keys overflow the sum (and move m) while masked ones give 0.
+          const float negm = -fmaxf(m, -3.0e38f);
+          float pv[16];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          mx0 = fmaxf(mx0, acc[i]);
-          mx1 = fmaxf(mx1, acc[i + 1]);
-        }
-        const float mnew = fmaxf(m, max_xor32(fmaxf(mx0, mx1)) * c_scale);
-        // m == mnew also covers lanes that have seen no key (both -inf).
-        const float alpha = m == mnew ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
-        l *= alpha;
-        lb *= alpha;
+          for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c_scale, negm));
+          float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        m = mnew;
+          for (int i = 0; i < 16; i += 2) {
+            s0 += pv[i];
+            s1 += pv[i + 1];
+          }
+          lt = s0 + s1;
+          pbh[0] = pack8<T>(pv);
+          pbh[1] = pack8<T>(pv + 8);
+          lbt = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            lbt = sum2_acc<T>(pbh[0][w], lbt);
+            lbt = sum2_acc<T>(pbh[1][w], lbt);
+          }
+        };
         weights();
-      }
-      l += lt;
-      lb += lbt;
-    };
-    // O^T += V^T P^T for half nb: A = V^T gathered transposed from the V
-    // tile (keys 32*nb + 16*cc + 8*hh + 0..7), B = this lane's weights.
-    auto pv_half = [&](const u32x4 (&pbh)[2], int nb) {
+        if (__any(!(lt <= 256.0f))) {
+          // Keeps this rarely taken block a real branch: without it the
+          // compiler if-converts it and rescales the accumulator every time.
+          asm volatile("" ::: "memory");
+          float mx0 = acc[0], mx1 = acc[1];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const uint16_t* vk = vt + (32 * nb + 16 * cc) * D;
+          for (int i = 0; i < 16; i += 2) {
+            mx0 = fmaxf(mx0, acc[i]);
+            mx1 = fmaxf(mx1, acc[i + 1]);
+          }
+          const float mnew = fmaxf(m, max_xor32(fmaxf(mx0, mx1)) * c_scale);
+          // m == mnew also covers lanes that have seen no key (both -inf).
+          const float alpha = m == mnew ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+          l *= alpha;
+          lb *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          m = mnew;
+          weights();
+        }
+        l += lt;
+        lb += lbt;
+      };
+      // O^T += V^T P^T for half nb: A = V^T gathered transposed from the V
+      // tile (keys 32*nb + 16*cc + 8*hh + 0..7), B = this lane's weights.
+      auto pv_half = [&](const u32x4 (&pbh)[2], int nb) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const uint16_t* vk = vt + (32 * nb + 16 * cc) * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = mfma32x32x16<T>(lds_tr16(vk, v_off[0][db], v_off[1][db]), pbh[cc], oacc[db]);
+        }
+      };
+      f32x16 s0 = s_half(0);
+      mask_half(s0, 0);
+      f32x16 s1 = s_half(1);
+      u32x4 p0[2], p1[2];
+      soft_half(s0, p0);
+      mask_half(s1, 1);
+      pv_half(p0, 0);
+      soft_half(s1, p1);
+      pv_half(p1, 1);
+    };
+
+    auto step = [&](auto bufc, int j) {
+      constexpr int BUF = decltype(bufc)::value;
+      const int kv0 = j * BC + 64 * g;  // this wave's 64 keys of the tile
+      if (j + 1 < ntiles) load_tile(IntC<BUF ^ 1>{}, j + 1);
+      // Causal: tiles entirely above this wave's rows carry no weight for it.
+      if (!CAUSAL || kv0 <= q0 + 31 + off) {
+        const bool need_mask = (kv0 + 64 > Nk) || (CAUSAL && kv0 + 63 > q0 + off);
+        if (need_mask) {
+          compute(bufc, IntC<1>{}, kv0);
+        } else {
+          compute(bufc, IntC<0>{}, kv0);
+        }
+      }
+      tile_barrier();
+    };
+
+    load_tile(IntC<0>{}, 0);
+    tile_barrier();
+    for (int j = 0; j < ntiles; j += 2) {
+      step(IntC<0>{}, j);
+      if (j + 1 < ntiles) step(IntC<1>{}, j + 1);
+    }
+
+    if constexpr (SPLIT) {
+      // Merge the two key groups' (m, l, lb, O~) of each row through LDS: the
+      // group-1 wave hands its lane values to the group-0 wave with the same
+      // rows (same lane layout).  The K/V buffers are free after the last
+      // tile barrier.  Layout [wave][value][lane], one array per d block of O~.
+      float* const xb[4] = {reinterpret_cast<float*>(Ks0), reinterpret_cast<float*>(Ks1),
+                            reinterpret_cast<float*>(Vs0), reinterpret_cast<float*>(Vs1)};
+      static_assert(DB <= 4 && Cfg::RW * 16 * 64 * 4 <= TILE * 2,
+                    "O~ exchange must fit a tile buffer");
+      float* const xs = xb[DB % 4] + (DB == 4 ? Cfg::RW * 16 * 64 : 0);
+      static_assert(Cfg::RW * 16 * 64 * 4 * (DB == 4 ? 1 : 0) + Cfg::RW * 3 * 64 * 4 <= TILE * 2,
+                    "scalar exchange must fit");
+      if (g == 1) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          oacc[db] = mfma32x32x16<T>(lds_tr16(vk, v_off[0][db], v_off[1][db]), pbh[cc], oacc[db]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xb[db][(rw * 16 + i) * 64 + lane] = oacc[db][i];
+        xs[(rw * 3 + 0) * 64 + lane] = m;
+        xs[(rw * 3 + 1) * 64 + lane] = l;
+        xs[(rw * 3 + 2) * 64 + lane] = lb;
       }
-    };
-    f32x16 s0 = s_half(0);
-    mask_half(s0, 0);
-    f32x16 s1 = s_half(1);
-    u32x4 p0[2], p1[2];
-    soft_half(s0, p0);
-    mask_half(s1, 1);
-    pv_half(p0, 0);
-    soft_half(s1, p1);
-    pv_half(p1, 1);
-  };
-
-  auto step = [&](auto bufc, int j) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int kv0 = j * BC + 64 * g;  // this wave's 64 keys of the tile
-    if (j + 1 < ntiles) load_tile(IntC<BUF ^ 1>{}, j + 1);
-    // Causal: tiles entirely above this wave's rows carry no weight for it.
-    if (!CAUSAL || kv0 <= q0 + 31 + off) {
-      const bool need_mask = (kv0 + 64 > Nk) || (CAUSAL && kv0 + 63 > q0 + off);
-      if (need_mask) {
-        compute(bufc, IntC<1>{}, kv0);
-      } else {
-        compute(bufc, IntC<0>{}, kv0);
+      __syncthreads();
+      if (g == 0) {
+        const float m1 = xs[(rw * 3 + 0) * 64 + lane];
+        const float mn = fmaxf(m, m1);
+        // m == mn also covers rows neither group has seen a key for.
+        const float a0 = m == mn ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+        const float a1 = m1 == mn ? 1.0f : __builtin_amdgcn_exp2f(m1 - mn);
+        l = l * a0 + xs[(rw * 3 + 1) * 64 + lane] * a1;
+        lb = lb * a0 + xs[(rw * 3 + 2) * 64 + lane] * a1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            oacc[db][i] = oacc[db][i] * a0 + xb[db][(rw * 16 + i) * 64 + lane] * a1;
+        m = mn;
       }
     }
-    tile_barrier();
-  };
 
-  load_tile(IntC<0>{}, 0);
-  tile_barrier();
-  for (int j = 0; j < ntiles; j += 2) {
-    step(IntC<0>{}, j);
-    if (j + 1 < ntiles) step(IntC<1>{}, j + 1);
-  }
-
-  if constexpr (SPLIT) {
-    // Merge the two key groups' (m, l, lb, O~) of each row through LDS: the
-    // group-1 wave hands its lane values to the group-0 wave with the same
-    // rows (same lane layout).  The K/V buffers are free after the last
-    // tile barrier.  Layout [wave][value][lane], one array per d block of O~.
-    float* const xb[4] = {reinterpret_cast<float*>(Ks0), reinterpret_cast<float*>(Ks1),
-                          reinterpret_cast<float*>(Vs0), reinterpret_cast<float*>(Vs1)};
-    static_assert(DB <= 4 && Cfg::RW * 16 * 64 * 4 <= TILE * 2, "O~ exchange must fit a tile buffer");
-    float* const xs = xb[DB % 4] + (DB == 4 ? Cfg::RW * 16 * 64 : 0);
-    static_assert(Cfg::RW * 16 * 64 * 4 * (DB == 4 ? 1 : 0) + Cfg::RW * 3 * 64 * 4 <= TILE * 2,
-                  "scalar exchange must fit");
-    if (g == 1) {
+    // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
+    // O is normalised by the sum of the weights exactly as the PV product used
+    // them (rounded to the input type), so each output row is a convex
+    // combination of V rows; the LSE uses the unrounded fp32 sum.
+    // A row that saw no key (possible only when N_q > N_k) has l = 0: O = 0,
+    // LSE = -inf.
+    const float lt = sum_xor32(l);
+    const float lbs = sum_xor32(lb);
+    const float inv = lbs > 0.0f ? __builtin_amdgcn_rcpf(lbs) : 0.0f;
+    if (g == 0 && qrow < N) {
+      uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xb[db][(rw * 16 + i) * 64 + lane] = oacc[db][i];
-      xs[(rw * 3 + 0) * 64 + lane] = m;
-      xs[(rw * 3 + 1) * 64 + lane] = l;
-      xs[(rw * 3 + 2) * 64 + lane] = lb;
-    }
-    __syncthreads();
-    if (g == 0) {
-      const float m1 = xs[(rw * 3 + 0) * 64 + lane];
-      const float mn = fmaxf(m, m1);
-      // m == mn also covers rows neither group has seen a key for.
-      const float a0 = m == mn ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-      const float a1 = m1 == mn ? 1.0f : __builtin_amdgcn_exp2f(m1 - mn);
-      l = l * a0 + xs[(rw * 3 + 1) * 64 + lane] * a1;
-      lb = lb * a0 + xs[(rw * 3 + 2) * 64 + lane] * a1;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          oacc[db][i] = oacc[db][i] * a0 + xb[db][(rw * 16 + i) * 64 + lane] * a1;
-      m = mn;
-    }
-  }
-
-  // Epilogue: O = O~ / l (one division per row), LSE = ln(sum exp(scale s)).
-  // O is normalised by the sum of the weights exactly as the PV product used
-  // them (rounded to the input type), so each output row is a convex
-  // combination of V rows; the LSE uses the unrounded fp32 sum.
-  // A row that saw no key (possible only when N_q > N_k) has l = 0: O = 0,
-  // LSE = -inf.
-  const float lt = sum_xor32(l);
-  const float lbs = sum_xor32(lb);
-  const float inv = lbs > 0.0f ? __builtin_amdgcn_rcpf(lbs) : 0.0f;
-  if (g == 0 && qrow < N) {
-    uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * hh;
-        const u32x2 v = {pack2<T>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                         pack2<T>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d) = v;
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * hh;
+          const u32x2 v = {pack2<T>(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                           pack2<T>(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d) = v;
+        }
+      }
+      if (hh == 0) {
+        p.lse[static_cast<int64_t>(bh) * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
       }
     }
-    if (hh == 0) {
-      p.lse[static_cast<int64_t>(bh) * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
-    }
-  }
   };  // run_block
 
   run_block(blk_hi);
