@@ -53,8 +53,9 @@ typedef enum {
                              causal not 0/1, unknown dtype, workspace too small */
   FA_ERR_UNSUPPORTED = 2, /* D not 64/128, tensor pointer not 16-byte aligned
                              (lse: 4-byte; workspace: 256-byte),
-                             b/n/h stride not a multiple of 8 elements, a
-                             size whose element offsets overflow int64, more
+                             b/n/h stride not a multiple of 8 elements, an
+                             n stride of 2^24 elements or more, a size
+                             whose element offsets overflow int64, more
                              than 2^31 rows B*H*N, or (fa_bwd) N*D*4 bytes
                              per head at or above 2^31 */
   FA_ERR_HIP = 3          /* a HIP runtime call failed (no device, launch error) */
@@ -224,7 +225,7 @@ int fa_merge(const void* o_parts, const float* lse_parts, int P, void* o,
  * is the logsumexp of the exact scaled scores (fp32 weights).  causal and
  * Nq != Nk: as fa_fwd_qk.  Strides (in elements, i.e. bytes for q, k, v)
  * as fa_fwd_strides or NULL for contiguous; q, k, v strides must be
- * multiples of 16 and their n strides below 2^24, o strides multiples of 8.
+ * multiples of 16, o strides multiples of 8, all n strides below 2^24.
  * Errors: as fa_fwd_qk; out_dtype other than FA_BF16 / FA_F16:
  * FA_ERR_INVALID_ARG.  Extra device memory: none.
  */

@@ -21,10 +21,13 @@ fa::Strides contiguous(int N, int H, int D) {
 fa::Strides from_abi(const fa_stride3& s) { return fa::Strides{s.b, s.n, s.h}; }
 
 // Strides must keep 16-byte alignment of every row start and must address
-// only non-negative offsets that fit int64.
+// only non-negative offsets that fit int64.  The kernels address one tile of
+// up to 128 rows with 32-bit element offsets, so the n stride stays below
+// 2^24 elements.
 int check_strides(const fa::Strides& s, int B, int N, int H, int D) {
   if (s.b < 0 || s.n < 0 || s.h < 0) return FA_ERR_UNSUPPORTED;
   if (s.b % 8 || s.n % 8 || s.h % 8) return FA_ERR_UNSUPPORTED;
+  if (s.n >= (int64_t{1} << 24)) return FA_ERR_UNSUPPORTED;
   // Largest element offset: (B-1)*sb + (N-1)*sn + (H-1)*sh + D-1.
   const double bound = static_cast<double>(B - 1) * s.b + static_cast<double>(N - 1) * s.n +
                        static_cast<double>(H - 1) * s.h + D;
@@ -155,7 +158,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   for (int i = 0; i < 3; ++i) {
     const fa::Strides& s = *s8[i];
     if ((st = check_strides(s, B, rows[i], H, D)) != FA_OK) return st;
-    if (s.b % 16 || s.n % 16 || s.h % 16 || s.n >= (int64_t{1} << 24)) return FA_ERR_UNSUPPORTED;
+    if (s.b % 16 || s.n % 16 || s.h % 16) return FA_ERR_UNSUPPORTED;
   }
   p.B = B;
   p.H = H;

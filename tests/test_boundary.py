@@ -225,6 +225,20 @@ def test_python_binding_checks_unequal_lengths_without_gpu():
                  torch.zeros(2, 1, 2, 17, dtype=torch.float32))
 
 
+def test_huge_n_stride_rejected():
+    """Tiles are addressed with 32-bit element offsets: n strides of 2^24
+    elements or more are refused before any launch, in every entry point."""
+    lib = _lib.load()
+    s = _lib.Stride3(64 * 2 * 64, 2 * 64, 64)
+    huge = _lib.Stride3(1 << 30, 1 << 24, 64)
+    fst = _lib.FwdStrides(s, huge, s, s)
+    assert lib.fa_fwd(P, P, P, P, P, 1, 2, 64, 64, 0, 0.125, _lib.FA_BF16,
+                      ctypes.byref(fst), None) == _lib.FA_ERR_UNSUPPORTED
+    bst = _lib.BwdStrides(s, s, s, s, s, s, s, huge)
+    assert lib.fa_bwd(P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0, 0.125, _lib.FA_BF16,
+                      ctypes.byref(bst), P, 1 << 30, None) == _lib.FA_ERR_UNSUPPORTED
+
+
 def test_fp8_rejects_before_launch():
     lib = _lib.load()
 
