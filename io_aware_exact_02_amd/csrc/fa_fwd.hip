@@ -25,11 +25,12 @@
 // tile is copied global -> LDS asynchronously while the current one is
 // consumed, so there is one barrier per tile.
 //
-// Causal head_dim-128 launches use the split form (FwdCfg SPLIT): two key
-// groups of waves share 128-key tiles, each workgroup runs a short and a
-// long query block (i and n-1-i), and the groups' partial results are merged
-// in LDS.  This evens out the work per workgroup, which otherwise grows with
-// the block index, at the cost of twice the K/V tile loads per query row.
+// Head_dim-128 launches use the split form (FwdCfg SPLIT): two key groups
+// of waves share 128-key tiles and their partial results are merged in LDS.
+// Causal workgroups run a short and a long query block (i and n-1-i), which
+// evens out the work per workgroup; non-causal ones get twice the waves of
+// the register-bound non-split kernel.  The cost is twice the K/V tile
+// loads per query row of a 256-row block.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -40,8 +41,8 @@ namespace fa {
 // the block against the g-th 64-key half of every tile, and the two partial
 // results of each row are merged exactly at the end (same rule as merging
 // attention over disjoint key sets).  A block has half the rows, so causal
-// launches can give every workgroup one short and one long block (see
-// launch_fwd_t).
+// launches can give every workgroup one short and one long block, and each
+// wave holds the state of one 32-row block only (see launch_fwd_t).
 template <int D, int NW, bool SPLIT = false>
 struct FwdCfg {
   static constexpr int KVG = SPLIT ? 2 : 1;  // key groups
@@ -415,19 +416,21 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Causal head_dim 128 from N = 1024 on: the split, paired form (about 10%
-// faster than one 256-row block per workgroup at N = 8192, where that
+// Head_dim 128 uses the split form: causal from N = 1024 on, paired (about
+// 10% faster than one 256-row block per workgroup at N = 8192, where that
 // launch has one workgroup per compute unit and the last blocks carry twice
-// the average work).  Otherwise 8 waves (256 query rows) per workgroup when
-// that still gives at least two workgroups per compute unit, else 4 waves
-// (128 rows).  The non-causal head_dim-128 kernel always uses 4 waves: at 8
-// it would not fit its registers into the two waves per SIMD an 8-wave
-// workgroup needs.  (The split form at head_dim 64 does not fit the 128
-// registers of its 4-waves-per-SIMD target and is not launched.)
+// the average work), and non-causal always (1.2-1.35x faster than 4 waves
+// of 32 rows each: the 8-wave non-split kernel does not fit its registers
+// into the two waves per SIMD an 8-wave workgroup needs, the split one does,
+// so a compute unit runs twice the waves).  Otherwise 8 waves (256 query
+// rows) per workgroup when that still gives at least two workgroups per
+// compute unit, else 4 waves (128 rows).  (The split form at head_dim 64
+// does not fit the 128 registers of its 4-waves-per-SIMD target and is not
+// launched.)
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  if constexpr (CAUSAL && D == 128) {
-    if (p.N >= 1024) return launch_fwd_nw<T, D, 8, CAUSAL, true>(p, s);
+  if constexpr (D == 128) {
+    if (!CAUSAL || p.N >= 1024) return launch_fwd_nw<T, D, 8, CAUSAL, true>(p, s);
   }
   if constexpr (D == 64 || CAUSAL) {
     const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
