@@ -168,3 +168,25 @@ def test_full_size_sampled(name, B, H, N, D):
         r = o8.fp8_rows(*_args(d), 0, h, rows, causal=True)
         assert np.max(np.abs(lse[0, h, rows] - r["LSE"])) <= LSE_TOL, f"{name} h{h} LSE"
         assert np.all(np.abs(o[0, rows, h] - r["O"]) <= r["bound"]), f"{name} h{h} O"
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1024, 1024), (1100, 1100), (1100, 1500), (1500, 1100)])
+def test_split_paired_head_dim_128(Nq, Nk):
+    """Causal head_dim-128 launches whose workgroups all fit on the device at
+    once run the split, paired form (two key groups merged in LDS, query
+    blocks i and n-1-i in one workgroup): even and odd block counts, and
+    rows that see no key.  Exact-weight inputs (tight bar) and random
+    inputs (the oracle's bound)."""
+    what = f"fp8 split Nq={Nq} Nk={Nk}"
+    _say("case", what)
+    d = fp8_exact_weight_inputs(1, Nq, Nk, 2, 128, 8800 + Nq + Nk)
+    o, lse = _run(d, True, d["scale"])
+    O, LSE = o8.attention_forward_fp8(*_args(d), causal=True, scale=d["scale"])
+    _check_lse_and_empty(o, lse, O, LSE, what)
+    vmax = np.abs(o8._descaled(d["v"], d["descale_v"])).max()
+    assert np.all(np.abs(o - O) <= 2.0 ** -8 * np.abs(O) + 1e-4 * vmax), what
+    d = fp8_random_inputs(1, Nq, Nk, 2, 128, 8900 + Nq + Nk)
+    o, lse = _run(d, True)
+    O, LSE = o8.attention_forward_fp8(*_args(d), causal=True)
+    _check_lse_and_empty(o, lse, O, LSE, what)
+    assert np.all(np.abs(o - O) <= o8.fp8_output_bound(*_args(d), causal=True)), what
