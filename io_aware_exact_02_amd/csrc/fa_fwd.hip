@@ -416,10 +416,12 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Head_dim 128 uses the split form: causal from N = 1024 on, paired (about
-// 10% faster than one 256-row block per workgroup at N = 8192, where that
-// launch has one workgroup per compute unit and the last blocks carry twice
-// the average work), and non-causal always (1.2-1.35x faster than 4 waves
+// Head_dim 128 uses the split form: causal from N = 1024 on when 256-row
+// blocks would give at most one workgroup per compute unit, paired (about
+// 10% faster at B1 H8 N8192, where the last blocks carry twice the average
+// work; with more workgroups than compute units later dispatch evens the
+// work out and the plain form, with half the K/V loads per row, is 11-17%
+// faster), and non-causal always (1.2-1.35x faster than 4 waves
 // of 32 rows each: the 8-wave non-split kernel does not fit its registers
 // into the two waves per SIMD an 8-wave workgroup needs, the split one does,
 // so a compute unit runs twice the waves).  Otherwise 8 waves (256 query
@@ -430,7 +432,8 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   if constexpr (D == 128) {
-    if (!CAUSAL || p.N >= 1024) return launch_fwd_nw<T, D, 8, CAUSAL, true>(p, s);
+    const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
+    if (!CAUSAL || (p.N >= 1024 && wg8 <= 256)) return launch_fwd_nw<T, D, 8, CAUSAL, true>(p, s);
   }
   if constexpr (D == 64 || CAUSAL) {
     const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
