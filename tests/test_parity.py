@@ -191,6 +191,30 @@ def test_config_c5_sampled():
         assert_grad("dV", got["dV"][b, :, h], dV[b, :, h], f"c5 head {h}")
 
 
+def test_causal_head_dim_128_wide():
+    """A causal head_dim-128 grid with more 256-row workgroups than compute
+    units (B=2 H=16 N=4096: 512) runs the plain 8-wave forward: O, LSE and dQ
+    at 64 sampled rows of every head, dK and dV in full on two heads."""
+    B, H, N = 2, 16, 4096
+    _say("case wide causal head_dim 128", B, H, N)
+    inp = random_qkv(B, N, H, 128, "bf16", seed=7800)
+    got = gpu_forward_backward(inp, True)
+    rows = sample_rows(N, 64, seed=7801)
+    for b in range(B):
+        for h in range(H):
+            r = oa.attention_rows(inp["q"], inp["k"], inp["v"], inp["do"], b, h, rows,
+                                  causal=True)
+            sub = {"O": got["O"][b, rows, h], "LSE": got["LSE"][b, h, rows]}
+            assert_forward(sub, r["O"], r["LSE"], f"b{b} h{h}")
+            assert_grad("dQ", got["dQ"][b, rows, h], r["dQ"], f"b{b} h{h}")
+    heads = [(0, 0), (1, H - 1)]
+    _, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=True,
+                                      heads=heads)
+    for (b, h) in heads:
+        assert_grad("dK", got["dK"][b, :, h], dK[b, :, h], f"b{b} h{h}")
+        assert_grad("dV", got["dV"][b, :, h], dV[b, :, h], f"b{b} h{h}")
+
+
 @pytest.mark.parametrize("name", ["s2048", "s4096", "s8192", "s4096c"])
 def test_pages_sweep_shapes(name):
     """The pages' speed-sweep shapes (B=2 H=8 D=64 fp16 [B,N,H,D]): O, LSE
