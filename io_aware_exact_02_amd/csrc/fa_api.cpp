@@ -110,6 +110,7 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.H = H;
   p.N = Nq;
   p.Nk = Nk;
+  p.off = Nk - Nq;
   const float c = std::fabs(scale) * 1.4426950408889634f;
   p.c = c > 1e-30f ? c : 1e-30f;
   p.negate_q = scale < 0.0f ? 1 : 0;

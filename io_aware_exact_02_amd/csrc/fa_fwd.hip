@@ -98,7 +98,7 @@ void fwd_kernel(FwdParams p) {
   const int h = bh % p.H;
   const int N = p.N;    // query rows
   const int Nk = p.Nk;  // keys; causal: query i sees keys j <= i + off
-  const int off = Nk - N;
+  const int off = p.off;
   const int g = SPLIT ? wave / Cfg::RW : 0;   // key group
   const int rw = SPLIT ? wave % Cfg::RW : wave;
 
@@ -431,15 +431,27 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
 // launched.)
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  if constexpr (D == 128) {
+  if constexpr (D == 64 && !CAUSAL) {
+    // Non-causal head_dim 64 runs the causal kernels with every key visible
+    // (mask offset Nk: no tile is skipped, only the key tail is masked).
+    // They fit the 128 registers of two 8-wave workgroups per compute unit
+    // (the non-causal instantiation needs about 170) and are 10-15% faster
+    // on large grids, 3% at B2 H12 N2048.
+    FwdParams q = p;
+    q.off = p.Nk;
+    return launch_fwd_t<T, D, true>(q, s);
+  } else {
     const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
-    if (!CAUSAL || (p.N >= 1024 && wg8 <= 256)) return launch_fwd_nw<T, D, 8, CAUSAL, true>(p, s);
+    if constexpr (D == 128 && !CAUSAL) {
+      return launch_fwd_nw<T, D, 8, false, true>(p, s);
+    } else {
+      if constexpr (D == 128) {
+        if (p.N >= 1024 && wg8 <= 256) return launch_fwd_nw<T, D, 8, true, true>(p, s);
+      }
+      if (wg8 >= 512) return launch_fwd_nw<T, D, 8, true>(p, s);
+      return launch_fwd_nw<T, D, 4, true>(p, s);
+    }
   }
-  if constexpr (D == 64 || CAUSAL) {
-    const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
-    if (wg8 >= 512) return launch_fwd_nw<T, D, 8, CAUSAL>(p, s);
-  }
-  return launch_fwd_nw<T, D, 4, CAUSAL>(p, s);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s) {

@@ -18,7 +18,8 @@ struct FwdParams {
   float* lse;  // [B, H, N] fp32
   Strides sq, sk, sv, so;
   int B, H, N;      // N: query rows
-  int Nk;           // keys (causal: query i sees keys j <= i + Nk - N)
+  int Nk;           // keys
+  int off;          // causal: query i sees keys j <= i + off (Nk - N)
   int num_qblocks;  // ceil(N / rows per workgroup)
   float c;          // |scale| * log2(e), at least 1e-30
   int negate_q;     // 1 when scale < 0: q enters the scores negated
