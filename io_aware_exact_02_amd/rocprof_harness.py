@@ -112,7 +112,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--raw", required=True, help="directory for raw rocprofv3 output")
     ap.add_argument("--workloads", default="c2,c3,c4,c5")
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--calib-mib", type=int, default=512)
     ap.add_argument("--summary-dir", default=None)
     ap.add_argument("--timeout", type=int, default=300)
@@ -142,11 +142,17 @@ def main(argv=None):
                 os.path.join(a.raw, f"pmc_{name}.log"))
         ctr[name] = counters_by_kernel(read_csv(os.path.join(out, "**", "*counter_collection.csv")))
 
-    # Durations per (kernel, grid) from the trace.
+    # Durations per (kernel, grid) from the trace, in dispatch order.  The
+    # bench launches each sweep kernel warmup + steps times; "timed" is the
+    # mean over the last `steps` dispatches, the ones bench.py times.
     dur = collections.defaultdict(list)
-    for r in trace:
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
         k = short_name(r["Kernel_Name"]) + f" grid={grid_size(r)}"
         dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+
+    def timed_avg(d):
+        tail = d[-a.steps:] if len(d) >= a.steps else d
+        return sum(tail) / len(tail)
 
     # Calibration: the elementwise kernel moves calib_mib MiB each way.
     calib = [k for k in ctr["fetch"] if "neg" in k.lower()]
@@ -169,7 +175,7 @@ def main(argv=None):
              f"calibration: elementwise kernel of {a.calib_mib} MiB read + write; counter scale "
              f"FETCH x{f_scale:.4f}, WRITE x{w_scale:.4f}" if f_scale else "calibration: none",
              "",
-             f"{'kernel (grid)':64s} {'calls':>5s} {'avg us':>9s} {'min us':>9s} "
+             f"{'kernel (grid)':64s} {'calls':>5s} {'avg us':>9s} {'timed us':>9s} {'min us':>9s} "
              f"{'MFMA TF/s':>9s} {'%peak':>6s} {'rd GB/s':>8s} {'wr GB/s':>8s}"]
     record = None
     for k in sorted(dur, key=lambda x: -sum(dur[x])):
@@ -187,7 +193,8 @@ def main(argv=None):
         wr_b = (sum(wr) / len(wr)) * 1024 * (w_scale or 1.0) if wr else None
         tf = flops / avg / 1e12 if avg > 0 else 0.0
         peak = PEAK_FP8_TFLOPS if "fwd8" in k else PEAK_TFLOPS
-        lines.append(f"{k[:64]:64s} {len(d):5d} {avg * 1e6:9.1f} {min(d) * 1e6:9.1f} "
+        lines.append(f"{k[:64]:64s} {len(d):5d} {avg * 1e6:9.1f} {timed_avg(d) * 1e6:9.1f} "
+                     f"{min(d) * 1e6:9.1f} "
                      f"{tf:9.1f} {100 * tf / peak:6.1f} "
                      f"{(rd_b / avg / 1e9) if rd_b else 0:8.1f} {(wr_b / avg / 1e9) if wr_b else 0:8.1f}")
         # The dominant kernel: the bf16 head_dim-64 causal dK/dV kernel (only
@@ -196,6 +203,7 @@ def main(argv=None):
                 and "BF16, 64" in k and "true" in k):
             record = {"kernel": k, "workload": "c5: B=1 H=16 N=16384 D=64 bf16 causal",
                       "avg_launch_us": avg * 1e6,
+                      "timed_avg_launch_us": timed_avg(d) * 1e6,
                       "fetch_bytes_per_launch": rd_b, "write_bytes_per_launch": wr_b,
                       "hbm_bytes_per_launch": (rd_b or 0) + (wr_b or 0),
                       "executed_mfma_flops_per_launch": flops,
