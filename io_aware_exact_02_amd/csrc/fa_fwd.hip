@@ -242,18 +242,19 @@ void fwd_kernel(FwdParams p) {
           float pv[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c_scale, negm));
-          float s0 = 0.0f, s1 = 0.0f;
+          float s0 = pv[0], s1 = pv[1];
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) {
+          for (int i = 2; i < 16; i += 2) {
             s0 += pv[i];
             s1 += pv[i + 1];
           }
           lt = s0 + s1;
           pbh[0] = pack8<T>(pv);
           pbh[1] = pack8<T>(pv + 8);
-          lbt = 0.0f;
+          lbt = sum2_acc<T>(pbh[0][0], 0.0f);
+          lbt = sum2_acc<T>(pbh[1][0], lbt);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
+          for (int w = 1; w < 4; ++w) {
             lbt = sum2_acc<T>(pbh[0][w], lbt);
             lbt = sum2_acc<T>(pbh[1][w], lbt);
           }
