@@ -20,6 +20,9 @@ Prints ONE JSON line.  Besides the headline value it carries
                  with HIP events on its own stream inside the timed region,
                  against the 2516.6 TFLOP/s dense MFMA peak;
   cpu_baseline : the fp64 CPU oracle timed on a bounded sample (c5 heads);
+  dq_atomics   : the same kernel's 32-bit dQ accumulator atomics per launch
+                 and their achieved rate over its launch time (these adds
+                 execute at the memory side and bound the backward);
   per_config   : forward / backward times and TFLOP/s per workload;
   memory_c3    : peak device memory of fused fwd+bwd vs an unfused S/P
                  PyTorch baseline at c3 (untimed pass);
@@ -64,6 +67,20 @@ def conv_flops(w):
     if w.causal:
         f /= 2
     return f, 2.5 * f
+
+
+def dq_atomic_adds(w) -> int:
+    """Number of 32-bit atomic adds one dK/dV launch issues into the dQ
+    accumulator.  Each workgroup owns a block of keys (256 at head_dim 64,
+    128 at head_dim 128) and adds its dS K contribution for every query row
+    from the first one that sees its first key (causal) or from row 0, to
+    the last row: D adds per row."""
+    bkv = 256 if w.D == 64 else 128
+    total = 0
+    for kb0 in range(0, w.N, bkv):
+        q_begin = kb0 if w.causal else 0
+        total += (w.N - q_begin) * w.D
+    return total * w.B * w.H
 
 
 def kernel_source_hash() -> str:
@@ -471,6 +488,8 @@ def main(argv=None):
             "shape": w.describe(),
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "bwd_dkdv_kernel_ms": round(dkdv_ms, 4),
+            "dq_atomic_adds": dq_atomic_adds(w),
+            "dq_atomic_g_per_s": round(dq_atomic_adds(w) / dkdv_ms / 1e6, 1),
             "fwd_tflops": round(c["fwd_f"] / fwd_ms / 1e9, 2),
             "bwd_tflops": round(c["bwd_f"] / bwd_ms / 1e9, 2),
             "fwd_pct_peak": round(100 * c["fwd_f"] / fwd_ms / 1e9 / PEAK_MFMA_TFLOPS, 2),
@@ -478,6 +497,7 @@ def main(argv=None):
         }
 
     roofline = None
+    atomics = None
     dom = next((c for c in cases if c["w"].name == DOMINANT), None)
     if dom is not None:
         dkdv_ms = per_config[DOMINANT]["bwd_dkdv_kernel_ms"]
@@ -489,6 +509,12 @@ def main(argv=None):
                     "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                     "traffic": traffic_record()}
+        adds = dq_atomic_adds(dom["w"])
+        atomics = {"kernel": "bwd_dkdv_kernel", "workload": dom["w"].describe(),
+                   "adds_per_launch": adds, "bytes_per_add": 4,
+                   "avg_launch_ms": dkdv_ms,
+                   "achieved_g_adds_per_s": round(adds / dkdv_ms / 1e6, 1),
+                   "achieved_payload_tb_per_s": round(4 * adds / dkdv_ms / 1e9, 3)}
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -544,6 +570,7 @@ def main(argv=None):
             "flops_per_step": flops_step},
         "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
         "roofline": roofline,
+        "dq_atomics": atomics,
         "cpu_baseline": cpu,
         "per_config": per_config,
         "memory_c3": memory,
