@@ -1,7 +1,7 @@
 """rocprofv3 harness: kernel times, MFMA utilisation and HBM traffic of the
 attention kernels, measured on ``bench.py``.
 
-    python -m io_aware_exact_02_amd.rocprof_harness --raw gpurun_out/prof \\
+    python -m io_aware_exact_02_amd.rocprof_harness --raw /tmp/prof \\
         [--workloads c2,c3,c4,c5] [--summary-dir profiles]
 
 Four rocprofv3 runs of ``bench.py`` (each its own process; counters never

@@ -1,8 +1,9 @@
 """Plain float64 CPU oracle for exact scaled-dot-product attention.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
-links this module; only the tests, the graft smoke check and the
-``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+links this module; only the tests, the smoke check
+(``__graft_entry__.smoke``) and the ``cpu_baseline`` leg of ``bench.py`` use
+it.  It shares no code with the HIP
 path.
 
 What it computes, and where the pages define it:

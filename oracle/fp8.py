@@ -1,8 +1,8 @@
 """FP8 (E4M3) attention forward for the oracle.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
-links this module; only the tests and the graft smoke check use it.  It
-shares no code with the HIP path.
+links this module; only the tests use it.  It shares no code with the HIP
+path.
 
 The FlashAttention IO-awareness article at 0539edu.com (sections
 "H100的FP8加速能力" and "未来展望：FlashAttention-3带来的新可能") says that
