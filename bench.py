@@ -33,6 +33,8 @@ Prints ONE JSON line.  Besides the headline value it carries
                  (B=1 H=2 N=16384 D=64 causal), forward + backward;
   fp8_forward  : the FP8 (E4M3) forward at the sweep's shapes against the
                  dense fp8 peak and the 16-bit forward, untimed by the step;
+  split_kv     : the forward of short query blocks against a long key
+                 history, whole key range per workgroup vs key splits;
   mha_layer    : forward + backward of the whole multi-head attention layer
                  (QKV projection, attention, output projection) with the
                  fused kernels against the same layer with standard fp16
@@ -298,8 +300,9 @@ def fp8_forward(torch, fa, per_config):
 def head_shard(torch, fa):
     """One GPU's share of c5 when its 16 heads are split over 8 GPUs (no
     exchange needed): B=1 H=2 N=16384 D=64 bf16 causal, forward + backward
-    through the C ABI, 10 timed steps after 3 warm-ups.  256 workgroups in
-    the backward and 128 in the forward: one GPU's view of head sharding."""
+    through the C ABI, 10 timed steps after 3 warm-ups.  128 workgroups in
+    the backward; the forward splits the keys (fa_fwd_split_count's choice)
+    because its 32-row waves alone would leave most of the device idle."""
     from workloads import Workload, make_inputs
     dev = torch.device("cuda")
     w = Workload("c5/8", 1, 2, 16384, 64, "bf16", True, "bnhd", 1005)
@@ -326,9 +329,58 @@ def head_shard(torch, fa):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / 10
     fwd_f, bwd_f = conv_flops(w)
-    return {"shape": w.describe(), "ms_per_step": round(ms, 4),
+    from io_aware_exact_02_amd import _lib
+    splits = int(_lib.load().fa_fwd_split_count(1, 2, w.N, w.N, 64, 1))
+    return {"shape": w.describe(), "fwd_key_splits": splits, "ms_per_step": round(ms, 4),
             "tflops": round((fwd_f + bwd_f) / ms / 1e9, 2),
             "pct_peak": round(100 * (fwd_f + bwd_f) / ms / 1e9 / PEAK_MFMA_TFLOPS, 2)}
+
+
+def split_kv(torch, fa):
+    """Forward of short query blocks against a long key history (one new row
+    per head, or a 512-row chunk of a long context), causal mask aligned to
+    the last key: the whole key range per workgroup (num_splits=1) against
+    the key-split forward at fa_fwd_split_count's choice (partial results
+    combined exactly by a second kernel).  10 timed launches after 3
+    warm-ups each.  ``kv_gb_per_s`` is the K and V bytes of one call over
+    the split time: these launches stream K and V once."""
+    from io_aware_exact_02_amd import _lib
+    from workloads import random_qkv
+    lib = _lib.load()
+    dev = torch.device("cuda")
+    shapes = [(1, 16, 1, 16384, 64), (1, 16, 512, 16384, 64), (8, 8, 1, 8192, 128)]
+
+    def timed(fn, iters=10, warm=3):
+        for _ in range(warm):
+            fn()
+        stream = torch.cuda.current_stream(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    rows = []
+    for i, (B, H, Nq, Nk, D) in enumerate(shapes):
+        qa = random_qkv(B, Nq, H, D, "bf16", 1200 + 2 * i)
+        ka = random_qkv(B, Nk, H, D, "bf16", 1201 + 2 * i)
+        q, k, v = qa["q"].to(dev), ka["k"].to(dev), ka["v"].to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+        S = int(lib.fa_fwd_split_count(B, H, Nq, Nk, D, 1))
+        t1 = timed(lambda: fa.fwd(q, k, v, causal=True, out=o, lse=lse, num_splits=1))
+        ts = timed(lambda: fa.fwd(q, k, v, causal=True, out=o, lse=lse, num_splits=S))
+        kv_bytes = 2 * B * H * Nk * D * 2
+        rows.append({"shape": f"B={B} H={H} Nq={Nq} Nk={Nk} D={D} bf16 causal",
+                     "num_splits": S, "unsplit_ms": round(t1, 4), "split_ms": round(ts, 4),
+                     "speedup": round(t1 / ts, 2),
+                     "kv_gb_per_s": round(kv_bytes / ts / 1e6, 1)})
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return rows
 
 
 def mha_layer(torch, fa):
@@ -397,6 +449,8 @@ def main(argv=None):
                     help="skip the standard-vs-fused forward sweep of the pages (N=2048..8192)")
     ap.add_argument("--no-mha", action="store_true", help="skip the attention-layer measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the key-split forward measurement")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the one-GPU share of c5 under 8-way head sharding")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -542,6 +596,10 @@ def main(argv=None):
     if not args.no_fp8:
         fp8 = fp8_forward(torch, fa, per_config)
 
+    splits = None
+    if not args.no_split:
+        splits = split_kv(torch, fa)
+
     layer = None
     if not args.no_mha:
         layer = mha_layer(torch, fa)
@@ -578,6 +636,7 @@ def main(argv=None):
         "mha_layer": layer,
         "fp8_forward": fp8,
         "head_shard_c5_of_8": shard,
+        "split_kv": splits,
         "device": {"name": torch.cuda.get_device_properties(0).name,
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
                    "derived_peak_tflops": round(

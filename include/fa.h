@@ -109,6 +109,43 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse,
               int dtype, const fa_fwd_strides* strides, hipStream_t stream);
 
 /*
+ * fa_fwd_split -- fa_fwd_qk with the keys divided among workgroups, for
+ * launches whose query side alone cannot fill the device (few heads, short
+ * Nq against a long key history, e.g. decoding or small chunks of a long
+ * context).  The keys are cut into contiguous ranges of ceil(Nk /
+ * num_splits) keys rounded up to a multiple of 128; every range is
+ * processed by its own workgroups, which write an fp32 partial (O_r, LSE_r)
+ * over that range into the workspace, and a second kernel combines them
+ * exactly with the rule of fa_merge (LSE = ln sum_r exp(LSE_r), O =
+ * sum_r exp(LSE_r - LSE) O_r), rounding o once.  The result is fa_fwd_qk's
+ * up to fp32 rounding of the combination; ranges a query row cannot see
+ * (causal) carry no weight.
+ *   num_splits      : 1 .. 256; 1 (or a count that leaves one range) is
+ *                     fa_fwd_qk and needs no workspace.
+ *   workspace       : device buffer of at least
+ *                     fa_fwd_split_workspace_bytes(B, H, Nq, D, num_splits)
+ *                     bytes, 256-byte aligned; contents undefined on entry
+ *                     and on exit.
+ * Other arguments and errors: as fa_fwd_qk; num_splits out of range, or a
+ * missing or too small workspace when it is needed: FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Nq, int Nk, int D, int causal, float scale,
+                 int dtype, const fa_fwd_strides* strides, int num_splits,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace of fa_fwd_split: fp32 [num_splits, B, H, Nq, D] partial outputs
+ * and [num_splits, B, H, Nq] logsumexps, each part rounded up to 256 bytes.
+ * Returns 0 for invalid sizes. */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
+
+/* A split count for fa_fwd_split: 1 unless the unsplit launch has at most
+ * one wave (32 query rows) per SIMD of the device and the keys allow splits
+ * of at least 2048; then enough splits for about four waves per SIMD, at
+ * most 64. */
+int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
+
+/*
  * fa_bwd_workspace_bytes -- size of the scratch fa_bwd needs: the row vector
  * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
  * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]

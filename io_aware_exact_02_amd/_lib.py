@@ -16,7 +16,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F16, FA_BF16 = 0, 1
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_qk", "fa_fwd_fp8", "fa_bwd", "fa_bwd_stages", "fa_bwd_qk",
+EXPORTS = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
+           "fa_fwd_split_count", "fa_fwd_fp8", "fa_bwd", "fa_bwd_stages", "fa_bwd_qk",
            "fa_bwd_workspace_bytes", "fa_bwd_qk_workspace_bytes", "fa_merge", "fa_status_str",
            "fa_version")
 STAGE_PREPROCESS, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
@@ -69,6 +70,13 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
                               ctypes.POINTER(FwdStrides), vp]
     lib.fa_fwd_qk.restype = i
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
+                                 ctypes.POINTER(FwdStrides), i, vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_split.restype = i
+    lib.fa_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_split_count.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_split_count.restype = i
     lib.fa_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
                               ctypes.POINTER(BwdStrides), vp, ctypes.c_size_t, ctypes.c_uint, vp]
     lib.fa_bwd_qk.restype = i

@@ -96,10 +96,14 @@ def _raise(status: int, what: str):
     raise RuntimeError(f"{what}: {msg}")
 
 
-def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
+def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None,
+        num_splits=None):
     """Forward pass.  q [B,Nq,H,D], k and v [B,Nk,H,D] (Nk = Nq for
     self-attention).  Returns (o [B,Nq,H,D], lse [B,H,Nq] fp32).  With
-    Nq != Nk the causal mask is aligned to the last query and key."""
+    Nq != Nk the causal mask is aligned to the last query and key.
+
+    num_splits: key splits (fa_fwd_split); None picks fa_fwd_split_count's
+    choice, 1 keeps the whole key range in each workgroup."""
     lib = _lib.load()
     B, N, Nk, H, D = _check_qkv(q, k, v)
     q, k, v = _usable(q), _usable(k), _usable(v)
@@ -111,13 +115,24 @@ def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise FaArgError("lse must be a contiguous float32 [B, H, N] tensor")
+    if num_splits is None:
+        num_splits = lib.fa_fwd_split_count(B, H, N, Nk, D, int(bool(causal)))
+    elif not isinstance(num_splits, int) or not 1 <= num_splits <= 256:
+        raise FaArgError(f"num_splits must be an int in 1..256, got {num_splits!r}")
     st = _lib.FwdStrides(_stride3(q), _stride3(k), _stride3(v), _stride3(out))
-    status = lib.fa_fwd_qk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr(), B, H, N, Nk, D, int(bool(causal)),
-                           _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
-                           _stream(q))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
+            Nk, D, int(bool(causal)), _scale(softmax_scale, D), _DTYPES[q.dtype],
+            ctypes.byref(st))
+    if num_splits > 1:
+        nbytes = int(lib.fa_fwd_split_workspace_bytes(B, H, N, D, num_splits))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        status = lib.fa_fwd_split(*args, num_splits, ws.data_ptr(), nbytes, _stream(q))
+        what = "fa_fwd_split"
+    else:
+        status = lib.fa_fwd_qk(*args, _stream(q))
+        what = "fa_fwd_qk"
     if status != _lib.FA_OK:
-        _raise(status, "fa_fwd_qk")
+        _raise(status, what)
     return out, lse
 
 

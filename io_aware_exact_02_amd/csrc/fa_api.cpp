@@ -73,11 +73,12 @@ BwdWorkspace bwd_workspace(int B, int H, int Nq, int Nk, int D) {
 }
 }  // namespace
 
-extern "C" {
-
-int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-              int Nq, int Nk, int D, int causal, float scale, int dtype,
-              const fa_fwd_strides* strides, hipStream_t stream) {
+namespace {
+// Validates the arguments of a 16-bit forward and fills the parameter block
+// for the whole key range (one split).
+int make_fwd_params(fa::FwdParams& p, const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int H, int Nq, int Nk, int D, int causal, float scale,
+                    int dtype, const fa_fwd_strides* strides) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   int st = check_sizes(B, H, Nq, D, causal, scale, dtype);
   if (st != FA_OK) return st;
@@ -85,7 +86,7 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_UNSUPPORTED;
-  fa::FwdParams p{};
+  p = fa::FwdParams{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -114,7 +115,117 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
   const float c = std::fabs(scale) * 1.4426950408889634f;
   p.c = c > 1e-30f ? c : 1e-30f;
   p.negate_q = scale < 0.0f ? 1 : 0;
+  p.num_splits = 1;
+  p.split_len = Nk;
+  return FA_OK;
+}
+
+constexpr int kMaxSplits = 256;
+
+// Keys per split for a requested split count: ceil(Nk / S) rounded up to a
+// multiple of 128 (the widest K/V tile), so that every split starts on a
+// tile boundary.
+int64_t split_len_for(int Nk, int S) {
+  const int64_t len = (static_cast<int64_t>(Nk) + S - 1) / S;
+  return (len + 127) / 128 * 128;
+}
+
+// Workspace of the key-split forward: fp32 partial outputs [S, B*H, Nq, D]
+// and their logsumexps [S, B*H, Nq], each part on a 256-byte boundary.
+struct SplitWorkspace {
+  size_t lse, total;
+};
+SplitWorkspace split_workspace(int B, int H, int Nq, int D, int S) {
+  const size_t rows = static_cast<size_t>(S) * B * H * Nq;
+  SplitWorkspace w{};
+  w.lse = align256(rows * D * sizeof(float));
+  w.total = w.lse + align256(rows * sizeof(float));
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int Nq, int Nk, int D, int causal, float scale, int dtype,
+              const fa_fwd_strides* strides, hipStream_t stream) {
+  fa::FwdParams p;
+  const int st = make_fwd_params(p, q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale, dtype,
+                                 strides);
+  if (st != FA_OK) return st;
   const hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || (D != 64 && D != 128)) return 0;
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  if (static_cast<int64_t>(B) * H * Nq > (int64_t{1} << 31) - 1) return 0;
+  return split_workspace(B, H, Nq, D, num_splits).total;
+}
+
+int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return 1;
+  // Waves of the unsplit launch: one per 32 query rows, two where head_dim
+  // 128 runs the two-key-group form (non-causal, or causal from 1024 rows
+  // when 256-row blocks leave CUs free; see launch_fwd).
+  int64_t waves = static_cast<int64_t>(B) * H * ((Nq + 31) / 32);
+  const int64_t wg256 = static_cast<int64_t>(B) * H * ((Nq + 255) / 256);
+  if (D == 128 && (!causal || (Nq >= 1024 && wg256 <= 256))) waves *= 2;
+  // Splitting pays when the launch has at most one wave per SIMD (1024 on
+  // 256 CUs) and every split keeps at least 2048 keys: then aim for four
+  // waves per SIMD.  Measured on MI355X: one query row per head against 16K
+  // keys runs 4x faster with 8 splits; B1 H2 N16384 causal 1.7x with 4;
+  // launches with more waves, or short key ranges (B2 H12 N512 or N2048),
+  // gain nothing because the partial results cost a pass over O in fp32.
+  if (waves > 1024) return 1;
+  int64_t s = (4096 + waves - 1) / waves;
+  s = s < Nk / 2048 ? s : Nk / 2048;
+  s = s < 64 ? s : 64;
+  return s > 1 ? static_cast<int>(s) : 1;
+}
+
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Nq, int Nk, int D, int causal, float scale, int dtype,
+                 const fa_fwd_strides* strides, int num_splits, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  fa::FwdParams p;
+  int st = make_fwd_params(p, q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale, dtype, strides);
+  if (st != FA_OK) return st;
+  const int64_t len = split_len_for(Nk, num_splits);
+  const int S = static_cast<int>((Nk + len - 1) / len);  // splits that hold keys
+  if (S > 1) {
+    if (!workspace) return FA_ERR_INVALID_ARG;
+    if (workspace_bytes < split_workspace(B, H, Nq, D, num_splits).total) return FA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_UNSUPPORTED;
+    // The grid (one workgroup per 32 query rows at most, per split) must fit.
+    if (static_cast<int64_t>(B) * H * ((Nq + 31) / 32) * S > (int64_t{1} << 31) - 1)
+      return FA_ERR_UNSUPPORTED;
+  }
+  if (S == 1) {
+    const hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  const SplitWorkspace w = split_workspace(B, H, Nq, D, num_splits);
+  char* ws = static_cast<char*>(workspace);
+  p.num_splits = S;
+  p.split_len = static_cast<int>(len);
+  p.o_part = reinterpret_cast<float*>(ws);
+  p.lse_part = reinterpret_cast<float*>(ws + w.lse);
+  hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  fa::SplitMergeParams m{};
+  m.o_part = p.o_part;
+  m.lse_part = p.lse_part;
+  m.o = p.o;
+  m.lse = p.lse;
+  m.so = p.so;
+  m.S = S;
+  m.B = B;
+  m.H = H;
+  m.N = Nq;
+  e = fa::launch_split_merge(m, dtype, D, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

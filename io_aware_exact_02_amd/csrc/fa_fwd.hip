@@ -104,8 +104,15 @@ void fwd_kernel(FwdParams p) {
 
   // Query blocks of this workgroup, heaviest first.  Causal split launches
   // pair block i with block n-1-i so that every workgroup does the same work.
+  // blockIdx.x = (ks * slots + slot) * BH + bh, with ks the key split: this
+  // workgroup sees keys [kv_lo, kv_hi) only.
   constexpr bool PAIRED = CAUSAL && SPLIT;
-  const int slot = static_cast<int>(blockIdx.x / BH);
+  const int slots = PAIRED ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
+  const int rest = static_cast<int>(blockIdx.x / BH);
+  const int slot = rest % slots;
+  const int ks = rest / slots;
+  const int kv_lo = ks * p.split_len;
+  const int kv_hi = Nk - kv_lo <= p.split_len ? Nk : kv_lo + p.split_len;
   const int blk_hi = p.num_qblocks - 1 - slot;
   const int nblk = PAIRED && slot != blk_hi ? 2 : 1;
 
@@ -163,16 +170,22 @@ void fwd_kernel(FwdParams p) {
     const float c_scale = p.c;
 
     const int qlast = min(qblk * BR + BR, N) - 1;
-    // Causal: up to the last key the workgroup's last row sees (at least one
-    // tile, so that rows seeing no key still go through the masked path).
-    const int ntiles = CAUSAL ? (max(min(qlast + off, Nk - 1), 0) / BC + 1) : ((Nk + BC - 1) / BC);
+    // Tiles t0 .. t0 + ntiles - 1 of this split's keys; causal: up to the
+    // last key the block's last row sees.  The first split runs at least one
+    // tile, so that rows seeing no key still go through the masked path; a
+    // later split none of whose keys the block sees runs no tile and leaves
+    // an empty partial result (O = 0, LSE = -inf).
+    const int t0 = kv_lo / BC;
+    const int last_key = CAUSAL ? min(qlast + off, kv_hi - 1) : kv_hi - 1;
+    const int ntiles = kv_lo == 0 ? max(last_key, 0) / BC + 1
+                                  : (last_key >= kv_lo ? (last_key - kv_lo) / BC + 1 : 0);
 
-    // Issue the loads of tile j into buffer BUF.  Rows past N (last tile only)
-    // are clamped to row N-1: those keys are masked, so their finite values
-    // never reach the result.
+    // Issue the loads of tile t0 + j into buffer BUF.  Rows past Nk (last
+    // tile only) are clamped to row Nk-1: those keys are masked, so their
+    // finite values never reach the result.
     auto load_tile = [&](auto bufc, int j) {
       constexpr int BUF = decltype(bufc)::value;
-      const int kv0 = j * BC;
+      const int kv0 = (t0 + j) * BC;
       const uint16_t* kt = kbase + static_cast<int64_t>(kv0) * p.sk.n;
       const uint16_t* vt = vbase + static_cast<int64_t>(kv0) * p.sv.n;
       const bool tail = kv0 + BC > Nk;
@@ -221,7 +234,7 @@ void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kv0 + 32 * nb + c_item(i, hh);
-            if (key >= Nk || (CAUSAL && key > qrow + off)) acc[i] = -INFINITY;
+            if (key >= kv_hi || (CAUSAL && key > qrow + off)) acc[i] = -INFINITY;
           }
         }
       };
@@ -307,11 +320,11 @@ void fwd_kernel(FwdParams p) {
 
     auto step = [&](auto bufc, int j) {
       constexpr int BUF = decltype(bufc)::value;
-      const int kv0 = j * BC + 64 * g;  // this wave's 64 keys of the tile
+      const int kv0 = (t0 + j) * BC + 64 * g;  // this wave's 64 keys of the tile
       if (j + 1 < ntiles) load_tile(IntC<BUF ^ 1>{}, j + 1);
       // Causal: tiles entirely above this wave's rows carry no weight for it.
       if (!CAUSAL || kv0 <= q0 + 31 + off) {
-        const bool need_mask = (kv0 + 64 > Nk) || (CAUSAL && kv0 + 63 > q0 + off);
+        const bool need_mask = (kv0 + 64 > kv_hi) || (CAUSAL && kv0 + 63 > q0 + off);
         if (need_mask) {
           compute(bufc, IntC<1>{}, kv0);
         } else {
@@ -321,8 +334,10 @@ void fwd_kernel(FwdParams p) {
       tile_barrier();
     };
 
-    load_tile(IntC<0>{}, 0);
-    tile_barrier();
+    if (ntiles > 0) {
+      load_tile(IntC<0>{}, 0);
+      tile_barrier();
+    }
     for (int j = 0; j < ntiles; j += 2) {
       step(IntC<0>{}, j);
       if (j + 1 < ntiles) step(IntC<1>{}, j + 1);
@@ -376,7 +391,21 @@ void fwd_kernel(FwdParams p) {
     const float lt = sum_xor32(l);
     const float lbs = sum_xor32(lb);
     const float inv = lbs > 0.0f ? __builtin_amdgcn_rcpf(lbs) : 0.0f;
-    if (g == 0 && qrow < N) {
+    if (g == 0 && qrow < N && p.o_part != nullptr) {
+      // Key-split launch: this split's normalised fp32 output and logsumexp.
+      const int64_t prow = (static_cast<int64_t>(ks) * BH + bh) * N + qrow;
+      float* orow = p.o_part + prow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 v = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                           oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g4 + 4 * hh) = v;
+        }
+      }
+      if (hh == 0) p.lse_part[prow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+    } else if (g == 0 && qrow < N) {
       uint16_t* orow = p.o + b * p.so.b + static_cast<int64_t>(qrow) * p.so.n + h * p.so.h;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -411,7 +440,7 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   p.num_qblocks = (p.N + BR - 1) / BR;
   // Causal split launches run blocks i and n-1-i in one workgroup.
   const int slots = CAUSAL && SPLIT ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * slots;
+  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * slots * p.num_splits;
   hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPLIT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();

@@ -23,6 +23,14 @@ struct FwdParams {
   int num_qblocks;  // ceil(N / rows per workgroup)
   float c;          // |scale| * log2(e), at least 1e-30
   int negate_q;     // 1 when scale < 0: q enters the scores negated
+  // Key splits: split s covers keys [s*split_len, min((s+1)*split_len, Nk)).
+  // With o_part set, each (split, query row) writes its fp32 partial output
+  // o_part[(s*B*H + b*H + h)*N + n][d] and natural-log logsumexp
+  // lse_part[(s*B*H + b*H + h)*N + n] instead of o and lse.
+  int num_splits;   // 1: the whole key range
+  int split_len;    // keys per split, a multiple of 128 (>= Nk when unsplit)
+  float* o_part;
+  float* lse_part;
 };
 
 // FP8 forward: q, k, v are OCP E4M3 codes (strides in elements = bytes),
@@ -74,12 +82,24 @@ struct MergeParams {
   int P, B, H, N;
 };
 
+// Exact merge of the fp32 partial results of a key-split forward (FwdParams
+// o_part / lse_part) into o and lse.
+struct SplitMergeParams {
+  const float* o_part;    // [S, B*H, N, D]
+  const float* lse_part;  // [S, B*H, N]
+  uint16_t* o;            // [B, N, H, D] with strides so
+  float* lse;             // [B, H, N]
+  Strides so;
+  int S, B, H, N;
+};
+
 // dtype: 0 = f16, 1 = bf16.  Return the launch status.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s);
 // stages: bit 0 preprocess, bit 1 dK/dV (+ dQ accumulation), bit 2 dQ conversion.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
                       hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_split_merge(const SplitMergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_fwd8(const Fwd8Params& p, int out_dtype, int D, int causal, hipStream_t s);
 
 }  // namespace fa

@@ -64,6 +64,68 @@ static hipError_t launch_merge_t(const MergeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The partial results of a key-split forward, fp32 and normalised per split:
+// the same rule over the splits, rounded to the output type once.  One row
+// (b, h, n) per D/8 threads, 8 elements each; splits that saw no key of the
+// row (LSE -inf) carry no weight.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeParams p) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int tid = threadIdx.x;
+  const int part = tid % TPR;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + tid / TPR;  // (b*H + h)*N + n
+  if (row >= rows) return;
+  const int n = static_cast<int>(row % p.N);
+  const int bh = static_cast<int>(row / p.N);
+  const int b = bh / p.H, h = bh % p.H;
+
+  float m = -INFINITY;
+  for (int s = 0; s < p.S; ++s) m = fmaxf(m, p.lse_part[s * rows + row]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (m > -INFINITY) {
+    float tot = 0.0f;
+    for (int s = 0; s < p.S; ++s) {
+      const float ls = p.lse_part[s * rows + row];
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+      tot += w;
+      const float* op = p.o_part + (s * rows + row) * D + part * 8;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(op);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(op + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * a0[e];
+        acc[e + 4] += w * a1[e];
+      }
+    }
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    lse = m + __builtin_logf(tot);
+  }
+  stg16(p.o + b * p.so.b + static_cast<int64_t>(n) * p.so.n + h * p.so.h + part * 8,
+        pack8<T>(acc));
+  if (part == 0) p.lse[row] = lse;
+}
+
+template <typename T, int D>
+static hipError_t launch_split_merge_t(const SplitMergeParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
+  const unsigned blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL((split_merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const SplitMergeParams& p, int dtype, int D, hipStream_t s) {
+  if (dtype == 1)
+    return D == 64 ? launch_split_merge_t<BF16, 64>(p, s) : launch_split_merge_t<BF16, 128>(p, s);
+  return D == 64 ? launch_split_merge_t<F16, 64>(p, s) : launch_split_merge_t<F16, 128>(p, s);
+}
+
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s) {
   if (dtype == 1) return D == 64 ? launch_merge_t<BF16, 64>(p, s) : launch_merge_t<BF16, 128>(p, s);
   return D == 64 ? launch_merge_t<F16, 64>(p, s) : launch_merge_t<F16, 128>(p, s);

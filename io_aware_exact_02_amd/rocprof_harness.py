@@ -80,7 +80,8 @@ def run(cmd, timeout, log):
 
 def bench_cmd(workloads, steps, calib_mib):
     return [sys.executable, BENCH, "--steps", str(steps), "--warmup", "2", "--cpu-seconds", "0",
-            "--no-memory", "--no-pages-sweep", "--no-mha", "--no-shard", "--workloads", workloads,
+            "--no-memory", "--no-pages-sweep", "--no-mha", "--no-shard", "--no-split",
+            "--workloads", workloads,
             "--copy-calibration-mib", str(calib_mib)]
 
 

@@ -277,3 +277,44 @@ def test_fp8_binding_checks_without_gpu():
     with pytest.raises(fa.FaArgError, match="differ"):
         fa.fwd_fp8(q, torch.zeros(1, 16, 3, 64, dtype=torch.uint8),
                    torch.zeros(1, 16, 3, 64, dtype=torch.uint8))
+
+
+def test_split_entry_points_without_launch():
+    """fa_fwd_split's host functions and argument errors.  Every call of
+    fa_fwd_split below is rejected before any HIP call (4096 keys with two
+    splits leave two key ranges, so the workspace is required)."""
+    lib = _lib.load()
+    a256 = lambda x: (x + 255) // 256 * 256
+    rows = 4 * 1 * 2 * 3  # S * B * H * Nq
+    assert lib.fa_fwd_split_workspace_bytes(1, 2, 3, 64, 4) == a256(4 * rows * 64) + a256(4 * rows)
+    for bad in [(1, 2, 3, 64, 0), (1, 2, 3, 64, 257), (1, 2, 3, 48, 2), (0, 2, 3, 64, 2)]:
+        assert lib.fa_fwd_split_workspace_bytes(*bad) == 0
+
+    # Split counts: launches with more than one wave per SIMD are not split
+    # (the four sweep workloads; head_dim-128 key-group forms count twice);
+    # narrow launches get splits of at least 2048 keys.
+    assert lib.fa_fwd_split_count(1, 16, 16384, 16384, 64, 1) == 1
+    assert lib.fa_fwd_split_count(1, 8, 8192, 8192, 128, 1) == 1
+    assert lib.fa_fwd_split_count(2, 12, 2048, 2048, 64, 0) == 1
+    assert lib.fa_fwd_split_count(2, 12, 512, 512, 64, 0) == 1
+    assert lib.fa_fwd_split_count(1, 8, 4096, 4096, 128, 1) == 1
+    assert lib.fa_fwd_split_count(1, 2, 16384, 16384, 64, 1) == 4
+    assert lib.fa_fwd_split_count(1, 16, 1, 16384, 64, 1) == 8
+    assert lib.fa_fwd_split_count(8, 8, 1, 8192, 128, 1) == 4
+    assert lib.fa_fwd_split_count(1, 16, 1, 2048, 64, 1) == 1
+    assert lib.fa_fwd_split_count(1, 1, 1, 500, 64, 0) == 1
+    assert lib.fa_fwd_split_count(0, 1, 1, 500, 64, 0) == 1
+
+    need = lib.fa_fwd_split_workspace_bytes(1, 1, 128, 64, 2)
+
+    def split(S=2, ws=P, wsb=1 << 40, Nq=128, Nk=4096, D=64):
+        return lib.fa_fwd_split(P, P, P, P, P, 1, 1, Nq, Nk, D, 0, 0.125, _lib.FA_BF16, None,
+                                S, ws, wsb, None)
+
+    assert split(S=0) == _lib.FA_ERR_INVALID_ARG
+    assert split(S=257) == _lib.FA_ERR_INVALID_ARG
+    assert split(ws=None) == _lib.FA_ERR_INVALID_ARG
+    assert split(wsb=need - 1) == _lib.FA_ERR_INVALID_ARG
+    assert split(ws=P + 16) == _lib.FA_ERR_UNSUPPORTED
+    assert split(D=48) == _lib.FA_ERR_UNSUPPORTED
+    assert split(Nq=0) == _lib.FA_ERR_INVALID_ARG
