@@ -25,6 +25,12 @@
 // tile is copied global -> LDS asynchronously while the current one is
 // consumed, so there is one barrier per tile.
 //
+// A launch may also divide the keys into contiguous ranges (FwdParams
+// num_splits, split_len): each workgroup then walks one range only and
+// writes an fp32 partial output and logsumexp, which a second kernel
+// (split_merge_kernel) combines exactly.  This serves launches whose query
+// side alone cannot fill the device.
+//
 // Head_dim-128 launches use the split form (FwdCfg SPLIT): two key groups
 // of waves share 128-key tiles and their partial results are merged in LDS.
 // Causal workgroups run a short and a long query block (i and n-1-i), which
