@@ -274,7 +274,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fa_status_str(int status);
 
-/* Library version string, e.g. "fa-gfx950 0.2.0" (static string). */
+/* Library version string, e.g. "fa-gfx950 0.3.0" (static string). */
 const char* fa_version(void);
 
 #ifdef __cplusplus

@@ -411,6 +411,6 @@ const char* fa_status_str(int status) {
   }
 }
 
-const char* fa_version(void) { return "fa-gfx950 0.2.0"; }
+const char* fa_version(void) { return "fa-gfx950 0.3.0"; }
 
 }  // extern "C"
