@@ -106,6 +106,36 @@ def test_scale_values(scale, causal):
     check_full(inp, causal, scale=scale, what=what)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_peaked_softmax(D, causal, dtype):
+    """Scores with a standard deviation of 16 to 23 (scale 2 on N(0,1)
+    inputs): nearly every row is dominated by a few keys, and the kernel's
+    lagging reference point moves on most tiles.  Forward and backward
+    against the oracle, over several tiles and a ragged tail.
+
+    Output bar: such rows are close to a single V row, so |O| reaches
+    max|v| (about 4.2 to 4.8 here), where rounding the exact result to bf16
+    alone costs up to 2^-8 |O| > 1e-2 (measured: the largest errors are
+    exactly the exact result's own bf16 rounding).  Element by element the
+    bar is the 1e-2 budget plus that rounding: |o - O| <= 1e-2 + 2^-8 |O|
+    (2^-11 |O| for fp16).  LSE and gradients keep the usual bars."""
+    what = f"peaked D={D} causal={causal} {dtype}"
+    _say("case", what)
+    inp = random_qkv(2, 333, 2, D, dtype, seed=7150 + D)
+    got = gpu_forward_backward(inp, causal, scale=2.0)
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=causal, scale=2.0)
+    rnd = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    over = np.abs(got["O"] - O) - (O_TOL + rnd * np.abs(O))
+    assert np.all(over <= 0), f"{what} O over the bar by {np.max(over):.3e}"
+    assert np.max(np.abs(got["LSE"] - LSE)) <= LSE_TOL, f"{what} LSE"
+    dQ, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"],
+                                       causal=causal, scale=2.0)
+    for name, ref in (("dQ", dQ), ("dK", dK), ("dV", dV)):
+        assert_grad(name, got[name], ref, what)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_strided_bhnd_input(D):
     """A [B,H,N,D] tensor passed through a transposed view (strides only)."""
