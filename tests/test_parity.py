@@ -136,6 +136,16 @@ def test_peaked_softmax(D, causal, dtype):
         assert_grad(name, got[name], ref, what)
 
 
+@pytest.mark.parametrize("D,causal,dtype", [(64, True, "bf16"), (128, False, "f16")])
+def test_many_short_heads(D, causal, dtype):
+    """B=16, H=32, N=100: 512 heads of one ragged tile each, several rounds of
+    workgroups per CU (head index decoding, backward key blocks)."""
+    what = f"many heads D={D} causal={causal} {dtype}"
+    _say("case", what)
+    inp = random_qkv(16, 100, 32, D, dtype, seed=7170 + D)
+    check_full(inp, causal, what=what)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_strided_bhnd_input(D):
     """A [B,H,N,D] tensor passed through a transposed view (strides only)."""
