@@ -35,6 +35,15 @@ int check_strides(const fa::Strides& s, int B, int N, int H, int D) {
   return FA_OK;
 }
 
+// B*H*N when every row index b*H*N + n fits 31 bits, else -1.  The product
+// is formed only after the division test, so it cannot overflow.
+int64_t rows_of(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return -1;
+  const int64_t heads = static_cast<int64_t>(B) * H;  // below 2^62
+  if (heads > ((int64_t{1} << 31) - 1) / N) return -1;
+  return heads * N;
+}
+
 int check_sizes(int B, int H, int N, int D, int causal, float scale, int dtype) {
   if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -42,9 +51,7 @@ int check_sizes(int B, int H, int N, int D, int causal, float scale, int dtype) 
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   // Row index b*H*N + n and the flattened grid must fit 32 bits.
-  const int64_t rows = static_cast<int64_t>(B) * H * N;
-  if (rows > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
-  if (rows * D > kI64Max / 8) return FA_ERR_UNSUPPORTED;
+  if (rows_of(B, H, N) < 0) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -158,14 +165,13 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
 }
 
 size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || (D != 64 && D != 128)) return 0;
+  if (rows_of(B, H, Nq) < 0 || (D != 64 && D != 128)) return 0;
   if (num_splits < 1 || num_splits > kMaxSplits) return 0;
-  if (static_cast<int64_t>(B) * H * Nq > (int64_t{1} << 31) - 1) return 0;
   return split_workspace(B, H, Nq, D, num_splits).total;
 }
 
 int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0) return 1;
+  if (rows_of(B, H, Nq) < 0 || Nk <= 0) return 1;
   // Waves of the unsplit launch: one per 32 query rows, two where head_dim
   // 128 runs the two-key-group form (non-causal, or causal from 1024 rows
   // when 256-row blocks leave CUs free; see launch_fwd).
@@ -288,7 +294,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || D <= 0) return 0;
+  if (rows_of(B, H, Nq) < 0 || rows_of(B, H, Nk) < 0 || (D != 64 && D != 128)) return 0;
   return bwd_workspace(B, H, Nq, Nk, D).total;
 }
 
@@ -383,7 +389,7 @@ int fa_merge(const void* o_parts, const float* lse_parts, int P, void* o, float*
   if (!o_parts || !lse_parts || !o || !lse || P <= 0) return FA_ERR_INVALID_ARG;
   int st = check_sizes(B, H, N, D, 0, 1.0f, dtype);
   if (st != FA_OK) return st;
-  if (static_cast<int64_t>(P) * B * H * N * D > kI64Max / 8) return FA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(P) > kI64Max / 8 / (rows_of(B, H, N) * D)) return FA_ERR_UNSUPPORTED;
   if (!aligned16(o_parts) || !aligned16(o)) return FA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(lse_parts) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)

@@ -318,3 +318,18 @@ def test_split_entry_points_without_launch():
     assert split(ws=P + 16) == _lib.FA_ERR_UNSUPPORTED
     assert split(D=48) == _lib.FA_ERR_UNSUPPORTED
     assert split(Nq=0) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_huge_sizes_do_not_overflow():
+    """Size products near the int range are rejected (or give 0 / 1) without
+    any intermediate overflow: B*H*N is compared by division first."""
+    lib = _lib.load()
+    big = (1 << 31) - 1
+    assert lib.fa_fwd_split_count(1 << 30, big, 4114, 129, 128, 1) == 1
+    assert lib.fa_fwd_split_workspace_bytes(big, big, big, 64, 2) == 0
+    assert lib.fa_bwd_qk_workspace_bytes(big, big, 2, 2, 64) == 0
+    assert lib.fa_bwd_qk_workspace_bytes(1, 1, 5, 5, 48) == 0
+    assert lib.fa_fwd_qk(P, P, P, P, P, big, big, big, big, 64, 0, 0.125, _lib.FA_BF16, None,
+                         None) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_merge(P, P, big, P, P, 1 << 15, 1 << 15, 1, 64, _lib.FA_BF16,
+                        None) == _lib.FA_ERR_UNSUPPORTED
