@@ -190,3 +190,32 @@ def test_split_paired_head_dim_128(Nq, Nk):
     O, LSE = o8.attention_forward_fp8(*_args(d), causal=True)
     _check_lse_and_empty(o, lse, O, LSE, what)
     assert np.all(np.abs(o - O) <= o8.fp8_output_bound(*_args(d), causal=True)), what
+
+
+def _fp8_random_cases(count, seed):
+    import random
+    rnd = random.Random(seed)
+    lengths = [1, 2, 31, 64, 65, 127, 128, 129, 200, 333, 513]
+    return [(i, rnd.randint(1, 3), rnd.randint(1, 4), rnd.choice(lengths), rnd.choice(lengths),
+             rnd.choice([64, 128]), rnd.random() < 0.5, rnd.choice(["bf16", "f16"]),
+             rnd.choice([None, 0.05, -0.09])) for i in range(count)]
+
+
+FP8_RANDOM = _fp8_random_cases(24, seed=20261204)
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nk,D,causal,out,scale", FP8_RANDOM,
+                         ids=[f"case{c[0]}" for c in FP8_RANDOM])
+def test_random_sample(i, B, H, Nq, Nk, D, causal, out, scale):
+    """A seeded random sample crossing lengths, head_dim, mask, output type
+    and scale (including negative ones) with per-head quantized inputs: O
+    within the oracle's elementwise bound, LSE <= 1e-3, empty rows exact."""
+    what = f"fp8 random {i}: B={B} H={H} Nq={Nq} Nk={Nk} D={D} causal={causal} {out} scale={scale}"
+    _say("case", what)
+    d = fp8_random_inputs(B, Nq, Nk, H, D, 12000 + i)
+    o, lse = _run(d, causal, scale, out)
+    O, LSE = o8.attention_forward_fp8(*_args(d), causal=causal, scale=scale)
+    _check_lse_and_empty(o, lse, O, LSE, what)
+    E = o8.fp8_output_bound(*_args(d), causal=causal, scale=scale)
+    over = np.abs(o - O) - E
+    assert np.all(over <= 0), f"{what}: O over the bound by {np.max(over):.3e}"
