@@ -119,8 +119,9 @@ def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None,
         num_splits = lib.fa_fwd_split_count(B, H, N, Nk, D, int(bool(causal)))
     elif not isinstance(num_splits, int) or not 1 <= num_splits <= 256:
         raise FaArgError(f"num_splits must be an int in 1..256, got {num_splits!r}")
-    st = _lib.FwdStrides(_stride3(q), _stride3(k), _stride3(v), _stride3(out))
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
+    out_u = _usable(out)
+    st = _lib.FwdStrides(_stride3(q), _stride3(k), _stride3(v), _stride3(out_u))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out_u.data_ptr(), lse.data_ptr(), B, H, N,
             Nk, D, int(bool(causal)), _scale(softmax_scale, D), _DTYPES[q.dtype],
             ctypes.byref(st))
     if num_splits > 1:
@@ -133,6 +134,8 @@ def fwd(q, k, v, causal: bool = False, softmax_scale=None, out=None, lse=None,
         what = "fa_fwd_qk"
     if status != _lib.FA_OK:
         _raise(status, what)
+    if out_u is not out:
+        out.copy_(out_u)
     return out, lse
 
 
@@ -248,7 +251,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, Nk, D,
             int(bool(causal)), _scale(softmax_scale, D), _DTYPES[q.dtype], ctypes.byref(st),
-            workspace.data_ptr(), workspace.numel())
+            workspace.data_ptr(), workspace.numel() * workspace.element_size())
     if stage_hook is None:
         status = lib.fa_bwd_qk(*args, _lib.STAGE_ALL, _stream(q))
         if status != _lib.FA_OK:

@@ -487,3 +487,26 @@ def test_no_quadratic_memory():
     nn = w.B * w.H * w.N * w.N * 2
     _say(f"extra {extra / 1e6:.1f} MB, allowed {allowed / 1e6:.1f} MB, one S matrix {nn / 1e9:.1f} GB")
     assert extra <= allowed
+
+
+def test_binding_output_and_workspace_layouts():
+    """fa.fwd into an output view the kernels cannot address directly (d
+    stride 2) stages through a contiguous buffer and copies back; fa.bwd
+    accepts a workspace of any element type, sized in bytes."""
+    _say("case binding layouts")
+    dev = torch.device("cuda")
+    inp = random_qkv(1, 150, 2, 64, "bf16", seed=7190)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = fa.fwd(q, k, v, causal=True)
+    wide = torch.full((1, 150, 2, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = wide[..., ::2]
+    o, lse = fa.fwd(q, k, v, causal=True, out=out)
+    nbytes = fa.workspace_bytes(1, 2, 150, 64)
+    ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=dev)
+    grads = fa.bwd(q, k, v, o_ref, lse_ref, do, causal=True, workspace=ws)
+    grads_ref = fa.bwd(q, k, v, o_ref, lse_ref, do, causal=True)
+    torch.cuda.synchronize()
+    assert o is out and torch.equal(out, o_ref) and torch.equal(lse, lse_ref)
+    assert torch.isnan(wide[..., 1::2]).all(), "wrote outside the output view"
+    for g, r in zip(grads, grads_ref):
+        assert torch.equal(g, r)
