@@ -78,8 +78,8 @@ def run(cmd, timeout, log):
         raise RuntimeError(f"exit {proc.returncode}: {' '.join(cmd)}\n{tail}")
 
 
-def bench_cmd(workloads, steps, calib_mib):
-    return [sys.executable, BENCH, "--steps", str(steps), "--warmup", "2", "--cpu-seconds", "0",
+def bench_cmd(workloads, steps, warmup, calib_mib):
+    return [sys.executable, BENCH, "--steps", str(steps), "--warmup", str(warmup), "--cpu-seconds", "0",
             "--no-memory", "--no-pages-sweep", "--no-mha", "--no-shard", "--no-split",
             "--workloads", workloads,
             "--copy-calibration-mib", str(calib_mib)]
@@ -114,6 +114,9 @@ def main(argv=None):
     ap.add_argument("--raw", required=True, help="directory for raw rocprofv3 output")
     ap.add_argument("--workloads", default="c2,c3,c4,c5")
     ap.add_argument("--steps", type=int, default=10)
+    # The same warm-up as bench.py's default: the GPU reaches its sustained
+    # clock state only after about a hundred steps.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--calib-mib", type=int, default=512)
     ap.add_argument("--summary-dir", default=None)
     ap.add_argument("--timeout", type=int, default=300)
@@ -121,7 +124,7 @@ def main(argv=None):
                     help="re-read the raw output of an earlier run instead of profiling")
     a = ap.parse_args(argv)
     os.makedirs(a.raw, exist_ok=True)
-    bench = bench_cmd(a.workloads, a.steps, a.calib_mib)
+    bench = bench_cmd(a.workloads, a.steps, a.warmup, a.calib_mib)
 
     t0 = time.time()
     if not a.summarize_only:
@@ -166,9 +169,9 @@ def main(argv=None):
         f_scale, w_scale = expect_kib / f_meas, expect_kib / w_meas
 
     lines = [f"rocprofv3 summary of bench.py --workloads {a.workloads} "
-             f"(steps {a.steps}, warmup 2)",
+             f"(steps {a.steps}, warmup {a.warmup})",
              "command: python -m io_aware_exact_02_amd.rocprof_harness --raw <dir> "
-             f"--workloads {a.workloads} --steps {a.steps} --calib-mib {a.calib_mib}",
+             f"--workloads {a.workloads} --steps {a.steps} --warmup {a.warmup} --calib-mib {a.calib_mib}",
              "  runs: rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py "
              + " ".join(bench[2:]),
              "        and the same command under rocprofv3 --pmc "
