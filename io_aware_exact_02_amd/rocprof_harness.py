@@ -14,7 +14,11 @@ share a run with tracing):
 3. ``--pmc FETCH_SIZE`` and 4. ``--pmc WRITE_SIZE``: bytes between L2 and
    memory (KiB per dispatch), each calibrated against one elementwise kernel
    of known size (one read and one write of ``--calib-mib`` MiB) run in the
-   same process.
+   same process;
+5. ``--kernel-trace --pmc`` of GRBM_GUI_ACTIVE and seven SQ counters: the
+   clock, matrix-core and VALU busy fractions, the share of wave cycles
+   spent waiting, and LDS activity and bank conflicts per kernel, written to
+   ``utilization_<workloads>.txt``.
 
 It prints the summary and, with ``--summary-dir``, writes
 ``kernels_<workloads>.txt`` (durations, executed MFMA TFLOP/s against the
@@ -100,6 +104,61 @@ def read_csv(pattern):
     return rows
 
 
+UTIL_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_BUSY_CU_CYCLES",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY",
+                 "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT"]
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def timed_counters(rows, steps):
+    """kernel -> {counter: mean over the kernel's last `steps` dispatches}.
+    Counter values are summed over all hardware instances (GRBM_GUI_ACTIVE
+    over the 8 XCDs, SQ counters over all CUs or SIMDs)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for r in rows:
+        k = short_name(r["Kernel_Name"]) + f" grid={grid_size(r)}"
+        per[k][r["Counter_Name"]][int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+    out = {}
+    for k, d in per.items():
+        out[k] = {}
+        for c, v in d.items():
+            vals = [v[i] for i in sorted(v)][-steps:]
+            out[k][c] = sum(vals) / len(vals)
+    return out
+
+
+def utilization_lines(rows, trace_rows, steps, kernels):
+    """Per kernel, from one --kernel-trace --pmc run (rocprof's derived-metric
+    formulas): clock = XCD cycles / duration; MFMA busy = MFMA busy cycles /
+    (SIMDs x cycles); VALU busy = 4 x VALU-active quad cycles / (SIMDs x
+    cycles); waiting = wave cycles waiting on anything / all wave cycles; LDS
+    active = LDS-index-active cycles / (CUs x cycles); bank conflicts as a
+    share of LDS-active cycles."""
+    ctr = timed_counters(rows, steps)
+    dur = collections.defaultdict(list)
+    for r in sorted(trace_rows, key=lambda r: int(r["Start_Timestamp"])):
+        k = short_name(r["Kernel_Name"]) + f" grid={grid_size(r)}"
+        dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    lines = [f"{'kernel (grid)':64s} {'us':>8s} {'GHz':>5s} {'MFMA%':>6s} {'VALU%':>6s} "
+             f"{'wait%':>6s} {'LDS%':>6s} {'bank%':>6s}"]
+    for k in kernels:
+        c = ctr.get(k)
+        d = dur.get(k)
+        if not c or not d or not c.get("GRBM_GUI_ACTIVE"):
+            continue
+        t = sum(d[-steps:]) / len(d[-steps:])
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+        pct = lambda x: 100.0 * x
+        lines.append(
+            f"{k[:64]:64s} {t * 1e6:8.1f} {cyc / t / 1e9:5.2f} "
+            f"{pct(c.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (SIMDS * cyc)):6.1f} "
+            f"{pct(4 * c.get('SQ_ACTIVE_INST_VALU', 0) / (SIMDS * cyc)):6.1f} "
+            f"{pct(c.get('SQ_WAIT_ANY', 0) / max(c.get('SQ_WAVE_CYCLES', 0), 1)):6.1f} "
+            f"{pct(c.get('SQ_LDS_IDX_ACTIVE', 0) / (CUS * cyc)):6.1f} "
+            f"{pct(c.get('SQ_LDS_BANK_CONFLICT', 0) / max(c.get('SQ_LDS_IDX_ACTIVE', 0), 1)):6.1f}")
+    return lines
+
+
 def counters_by_kernel(rows):
     """kernel -> {counter: [value per dispatch]}"""
     per = collections.defaultdict(lambda: collections.defaultdict(dict))
@@ -145,6 +204,13 @@ def main(argv=None):
             run(rocprof(["--pmc", *cs], out, bench), a.timeout,
                 os.path.join(a.raw, f"pmc_{name}.log"))
         ctr[name] = counters_by_kernel(read_csv(os.path.join(out, "**", "*counter_collection.csv")))
+
+    util_out = os.path.join(a.raw, "pmc_util")
+    if not a.summarize_only:
+        run(rocprof(["--kernel-trace", "--pmc", *UTIL_COUNTERS], util_out, bench), a.timeout,
+            os.path.join(a.raw, "pmc_util.log"))
+    util_rows = read_csv(os.path.join(util_out, "**", "*counter_collection.csv"))
+    util_trace = read_csv(os.path.join(util_out, "**", "*kernel_trace.csv"))
 
     # Durations per (kernel, grid) from the trace, in dispatch order.  The
     # bench launches each sweep kernel warmup + steps times; "timed" is the
@@ -227,12 +293,24 @@ def main(argv=None):
                      f"{sorted(stats[0].keys()) if stats else []})")
     text = "\n".join(lines)
     print(text)
+    sweep = [k for k in sorted(dur, key=lambda x: -sum(dur[x])) if "neg" not in k.lower()][:10]
+    util = "\n".join([
+        f"rocprofv3 utilization of bench.py --workloads {a.workloads} (steps {a.steps}, "
+        f"warmup {a.warmup}; means over each kernel's last {a.steps} dispatches)",
+        "command: python -m io_aware_exact_02_amd.rocprof_harness --raw <dir> "
+        f"--workloads {a.workloads} --steps {a.steps} --warmup {a.warmup} --calib-mib {a.calib_mib}",
+        "  run: rocprofv3 --kernel-trace --pmc " + " ".join(UTIL_COUNTERS)
+        + " --output-format csv -- python3 bench.py " + " ".join(bench[2:]),
+        "", *utilization_lines(util_rows, util_trace, a.steps, sweep)])
+    print(util)
     print(f"[harness] {time.time() - t0:.0f} s", flush=True)
     if a.summary_dir:
         os.makedirs(a.summary_dir, exist_ok=True)
         tag = a.workloads.replace(",", "-")
         with open(os.path.join(a.summary_dir, f"kernels_{tag}.txt"), "w") as f:
             f.write(text + "\n")
+        with open(os.path.join(a.summary_dir, f"utilization_{tag}.txt"), "w") as f:
+            f.write(util + "\n")
         if record is not None:
             with open(os.path.join(a.summary_dir, "traffic_bwd_dkdv_c5.json"), "w") as f:
                 json.dump(record, f, indent=1)
