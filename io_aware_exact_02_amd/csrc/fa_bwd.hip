@@ -253,8 +253,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) qt_off[t][db] = tr_off<D, true>(lane, t, db);
   // dS^T rows written by this wave: row 32*wave + l32, query chunk 2*(2qb+c) + hh.
-  const uint32_t ds_w = static_cast<uint32_t>((32 * wave + l32) * 2 * BQ +
-                                              16 * (hh ^ swz<BQ>(l32)));
+  // The 64-wide dS^T tile uses the store swizzle swz_st (conflict-free
+  // 128-bit stores); the 32-wide one keeps swz<32>.
+  constexpr bool DS_ST = BQ == 64;
+  int ds_sw;
+  if constexpr (DS_ST) {
+    ds_sw = swz_st(l32);
+  } else {
+    ds_sw = swz<BQ>(l32);
+  }
+  const uint32_t ds_w = static_cast<uint32_t>((32 * wave + l32) * 2 * BQ + 16 * (hh ^ ds_sw));
   // This wave's dQ blocks: transposed reads of dS (A) and K (B).
   uint32_t s_off[BPW][2], kt_off[BPW][2];
 #pragma unroll
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     const int blk = (wave + NW * bi) % NBLK;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      s_off[bi][t] = tr_off<BQ, false>(lane, t, blk / DB);
+      s_off[bi][t] = tr_off<BQ, false, DS_ST>(lane, t, blk / DB);
       kt_off[bi][t] = tr_off<D, false>(lane, t, blk % DB);
     }
   }

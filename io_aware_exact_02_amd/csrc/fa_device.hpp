@@ -190,6 +190,20 @@ __device__ __forceinline__ int swz(int r) {
     return ((u & 1) << 3) | ((u & 2) << 1) | ((u & 4) >> 1) | ((u & 8) >> 3);
   }
 }
+// Chunk swizzle of a width-64 tile that is written with ds_write_b128 (the
+// backward's dS^T tile).  gfx950 serves 128-bit LDS stores eight lanes at a
+// time across 128 bytes of banks, so the rows written by eight consecutive
+// lanes must use eight different chunks; swz<64> gives rows 2k and 2k+1 the
+// same chunk and was measured to spend 16% of the store cycles in bank
+// conflicts.  g(r) = (r % 8) ^ 4*((r / 2) % 2) permutes the chunks of every
+// eight rows, and rows r and r+2 differ in chunk bit 2, which keeps the
+// transposed reads (four consecutive rows, an aligned block of four logical
+// chunks) conflict-free as well (both measured: no conflict cycles).
+__device__ __forceinline__ int swz_st(int r) {
+  const int u = r & 7;
+  return u ^ ((u & 2) << 1);
+}
+
 // Element offset of (row r, column col) in a swizzled tile of width W.
 template <int W>
 __device__ __forceinline__ int tile_off(int r, int col) {
@@ -260,14 +274,17 @@ __device__ __forceinline__ uint32_t row_off(int lane, int kc) {
 }
 
 // tr_operand read t (0, 1) for k0 = 0, n0 = 32*j: add k0*2W for other k0
-// (a multiple of 16).  SIGMA: rows stored under sigma_row.
-template <int W, bool SIGMA>
+// (a multiple of 16).  SIGMA: rows stored under sigma_row.  ST: the tile
+// uses swz_st (width 64) instead of swz<W>.
+template <int W, bool SIGMA, bool ST = false>
 __device__ __forceinline__ uint32_t tr_off(int lane, int t, int j) {
+  static_assert(!ST || W == 64, "swz_st is defined for width 64");
   const int G = lane >> 4, s = lane & 15;
   int r = 8 * (G >> 1) + (s >> 2) + 4 * t;
   if constexpr (SIGMA) r = sigma32(r);
   const int col = 16 * (G & 1) + 4 * (s & 3);
-  const int off = r * 2 * W + ((((col >> 3) ^ swz<W>(r)) << 4) | ((col & 7) << 1));
+  const int sw = ST ? swz_st(r) : swz<W>(r);
+  const int off = r * 2 * W + ((((col >> 3) ^ sw) << 4) | ((col & 7) << 1));
   return static_cast<uint32_t>(off ^ (64 * j));
 }
 
