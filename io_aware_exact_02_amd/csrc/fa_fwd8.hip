@@ -83,6 +83,23 @@ struct Fwd8Occupancy {
   static constexpr int value = D == 64 ? 3 : 2;
 };
 
+// Chunk swizzle of the 8-bit K/V tiles (W = row length in 16-bit units).
+// With 64-byte rows (head_dim 64), four rows share a 256-byte bank line and
+// the transposing V reads gather eight consecutive rows per 16 lanes; 32
+// lanes then touch rows r and r+4 with the same pair of chunks under
+// swz<32>, a measured two-way conflict (a third of the kernel's LDS-active
+// cycles).  Swapping the two swizzle bits gives rows r and r+4 different
+// chunk pairs and keeps the row reads of K conflict-free (rows r, r+4, r+8,
+// r+12 still get four different chunks).  The period stays 16 rows.
+template <int W>
+__device__ __forceinline__ int swz8(int r) {
+  if constexpr (W == 32) {
+    return (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  } else {
+    return swz<W>(r);
+  }
+}
+
 template <typename T, int D, int NW, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(Fwd8Params p) {
@@ -161,7 +178,7 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        k_off[kc][t] = static_cast<uint32_t>(l32 * D + (((4 * kc + 2 * hh + t) ^ swz<W>(l32)) << 4));
+        k_off[kc][t] = static_cast<uint32_t>(l32 * D + (((4 * kc + 2 * hh + t) ^ swz8<W>(l32)) << 4));
     // A operand of O^T += V^T P^T for d block db: byte 8r + e of lane
     // (d = 32*db + l32, hh) is V[key 32*(r/2) + 16*(r%2) + 8*hh + e][d] -- the
     // key order of the weights in P (see the packing below).  Read r gathers
@@ -175,7 +192,7 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
       const int row = 8 * hh + (i >> 1);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        v_off[db] = static_cast<uint32_t>(row * D + (((2 * db + (G & 1)) ^ swz<W>(row)) << 4) +
+        v_off[db] = static_cast<uint32_t>(row * D + (((2 * db + (G & 1)) ^ swz8<W>(row)) << 4) +
                                           8 * (i & 1));
     }
     // Direct global -> LDS tile loads (one 16-byte slot per lane and call).
@@ -184,7 +201,7 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
     for (int it = 0; it < NCH; ++it) {
       const int slot = (wave + NW * it) * 64 + lane;
       const int pr = slot / CPR;
-      const int col = ((slot % CPR) ^ swz<W>(pr)) * 16;
+      const int col = ((slot % CPR) ^ swz8<W>(pr)) * 16;
       gk_off[it] = static_cast<uint32_t>(sigma_row(pr) * p.sk.n + col);
       gv_off[it] = static_cast<uint32_t>(pr * p.sv.n + col);
     }
@@ -216,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
           const int last = Nk - 1 - kv0;
           const int slot = (wave + NW * it) * 64 + lane;
           const int pr = slot / CPR;
-          const int col = ((slot % CPR) ^ swz<W>(pr)) * 16;
+          const int col = ((slot % CPR) ^ swz8<W>(pr)) * 16;
           ko = static_cast<uint32_t>(min(sigma_row(pr), last) * p.sk.n + col);
           vo = static_cast<uint32_t>(min(pr, last) * p.sv.n + col);
         }
