@@ -640,7 +640,10 @@ def main(argv=None):
         "fp8_forward": fp8,
         "head_shard_c5_of_8": shard,
         "split_kv": splits,
-        "device": {"name": torch.cuda.get_device_properties(0).name,
+        # The marketing name can be empty where the driver's id table is not
+        # installed; the architecture name is always there.
+        "device": {"name": torch.cuda.get_device_properties(0).name
+                   or getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
                    "derived_peak_tflops": round(
                        torch.cuda.get_device_properties(0).multi_processor_count
