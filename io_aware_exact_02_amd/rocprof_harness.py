@@ -172,7 +172,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--raw", required=True, help="directory for raw rocprofv3 output")
     ap.add_argument("--workloads", default="c2,c3,c4,c5")
-    ap.add_argument("--steps", type=int, default=10)
+    # The bench's own timed region: its average then matches the bench's events.
+    ap.add_argument("--steps", type=int, default=200)
     # The same warm-up as bench.py's default: the GPU reaches its sustained
     # clock state only after about a hundred steps.
     ap.add_argument("--warmup", type=int, default=100)
