@@ -31,6 +31,9 @@
 // (split_merge_kernel) combines exactly.  This serves launches whose query
 // side alone cannot fill the device.
 //
+// This kernel serves head_dim 128; head_dim 64 runs the software-pipelined
+// fwd64_kernel (fa_fwd64.hip), which keeps this data layout.
+//
 // Head_dim-128 launches use the split form (FwdCfg SPLIT): two key groups
 // of waves share 128-key tiles and their partial results are merged in LDS.
 // Causal workgroups run a short and a long query block (i and n-1-i), which
@@ -61,11 +64,10 @@ struct FwdCfg {
   static_assert(NCH * THREADS == BC * CPR, "tile load must divide evenly");
 };
 
-// Occupancy target in waves per SIMD.  The head_dim-64 forward is bound by
-// its softmax VALU work and needs several waves to overlap it with the
-// matrix cores, so the causal 8-wave kernel targets 4 waves (128 VGPRs).
-// Every other instantiation takes the highest target that compiles without
-// spilling (the non-causal kernels hold more live registers).
+// Occupancy target in waves per SIMD: the highest target that compiles
+// without spilling (the non-causal kernels hold more live registers).  The
+// head_dim-64 values are those of the earlier head_dim-64 launches of this
+// kernel; head_dim 64 now runs fwd64_kernel.
 template <int D, int NW, bool CAUSAL>
 struct FwdOccupancy {
   static constexpr int value = D == 64 ? (NW == 8 && CAUSAL ? 4 : 2) : (CAUSAL ? 2 : 1);
@@ -452,51 +454,34 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Head_dim 128 uses the split form: causal from N = 1024 on when 256-row
-// blocks would give at most one workgroup per compute unit, paired (about
-// 10% faster at B1 H8 N8192, where the last blocks carry twice the average
-// work; with more workgroups than compute units later dispatch evens the
-// work out and the plain form, with half the K/V loads per row, is 11-17%
-// faster), and non-causal always (1.2-1.35x faster than 4 waves
-// of 32 rows each: the 8-wave non-split kernel does not fit its registers
-// into the two waves per SIMD an 8-wave workgroup needs, the split one does,
-// so a compute unit runs twice the waves).  Otherwise 8 waves (256 query
-// rows) per workgroup when that still gives at least two workgroups per
-// compute unit, else 4 waves (128 rows).  (The split form at head_dim 64
-// does not fit the 128 registers of its 4-waves-per-SIMD target and is not
-// launched.)
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  if constexpr (D == 64 && !CAUSAL) {
-    // Non-causal head_dim 64 runs the causal kernels with every key visible
-    // (mask offset Nk: no tile is skipped, only the key tail is masked).
-    // They fit the 128 registers of two 8-wave workgroups per compute unit
-    // (the non-causal instantiation needs about 170) and are 10-15% faster
-    // on large grids, 3% at B2 H12 N2048.
-    FwdParams q = p;
-    q.off = p.Nk;
-    return launch_fwd_t<T, D, true>(q, s);
+// Head_dim 128 (head_dim 64 runs fwd64_kernel, fa_fwd64.hip) uses the split
+// form: causal from N = 1024 on when 256-row blocks would give at most one
+// workgroup per compute unit, paired (about 10% faster at B1 H8 N8192, where
+// the last blocks carry twice the average work; with more workgroups than
+// compute units later dispatch evens the work out and the plain form, with
+// half the K/V loads per row, is 11-17% faster), and non-causal always
+// (1.2-1.35x faster than 4 waves of 32 rows each: the 8-wave non-split
+// kernel does not fit its registers into the two waves per SIMD an 8-wave
+// workgroup needs, the split one does, so a compute unit runs twice the
+// waves).  Otherwise 8 waves (256 query rows) per workgroup when that still
+// gives at least two workgroups per compute unit, else 4 waves (128 rows).
+template <typename T, bool CAUSAL>
+static hipError_t launch_fwd128(const FwdParams& p, hipStream_t s) {
+  constexpr int D = 128;
+  const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
+  if constexpr (!CAUSAL) {
+    return launch_fwd_nw<T, D, 8, false, true>(p, s);
   } else {
-    const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
-    if constexpr (D == 128 && !CAUSAL) {
-      return launch_fwd_nw<T, D, 8, false, true>(p, s);
-    } else {
-      if constexpr (D == 128) {
-        if (p.N >= 1024 && wg8 <= 256) return launch_fwd_nw<T, D, 8, true, true>(p, s);
-      }
-      if (wg8 >= 512) return launch_fwd_nw<T, D, 8, true>(p, s);
-      return launch_fwd_nw<T, D, 4, true>(p, s);
-    }
+    if (p.N >= 1024 && wg8 <= 256) return launch_fwd_nw<T, D, 8, true, true>(p, s);
+    if (wg8 >= 512) return launch_fwd_nw<T, D, 8, true>(p, s);
+    return launch_fwd_nw<T, D, 4, true>(p, s);
   }
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s) {
-  if (dtype == 1) {
-    if (D == 64) return causal ? launch_fwd_t<BF16, 64, true>(p, s) : launch_fwd_t<BF16, 64, false>(p, s);
-    return causal ? launch_fwd_t<BF16, 128, true>(p, s) : launch_fwd_t<BF16, 128, false>(p, s);
-  }
-  if (D == 64) return causal ? launch_fwd_t<F16, 64, true>(p, s) : launch_fwd_t<F16, 64, false>(p, s);
-  return causal ? launch_fwd_t<F16, 128, true>(p, s) : launch_fwd_t<F16, 128, false>(p, s);
+  if (D == 64) return launch_fwd64(p, dtype, causal != 0, s);
+  if (dtype == 1) return causal ? launch_fwd128<BF16, true>(p, s) : launch_fwd128<BF16, false>(p, s);
+  return causal ? launch_fwd128<F16, true>(p, s) : launch_fwd128<F16, false>(p, s);
 }
 
 }  // namespace fa

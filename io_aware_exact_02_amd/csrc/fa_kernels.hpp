@@ -95,6 +95,8 @@ struct SplitMergeParams {
 
 // dtype: 0 = f16, 1 = bf16.  Return the launch status.
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int causal, hipStream_t s);
+// The software-pipelined head_dim-64 forward (fa_fwd64.hip); same contract.
+hipError_t launch_fwd64(const FwdParams& p, int dtype, bool causal, hipStream_t s);
 // stages: bit 0 preprocess, bit 1 dK/dV (+ dQ accumulation), bit 2 dQ conversion.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
                       hipStream_t s);
