@@ -13,7 +13,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The
- *   library never allocates, frees or keeps a pointer after it returns.
+ *   library never allocates, frees or keeps a pointer after it returns
+ *   (fa_bwd_noalloc's static scratch array, below, is the one piece of
+ *   device memory the library itself holds).
  * - Work is enqueued asynchronously on `stream` (NULL = the null stream).
  *   The library never synchronises; kernel faults surface at the caller's
  *   next synchronisation, as usual in HIP.
@@ -33,7 +35,9 @@
  *   before any HIP call and leave every buffer untouched.  The functions
  *   never print and never abort.
  * - Stateless and reentrant; concurrent calls on different streams are safe
- *   as long as their output and workspace buffers do not overlap.
+ *   as long as their output and workspace buffers do not overlap.  The
+ *   exception is fa_bwd_noalloc: its calls share one scratch array per
+ *   device and must not overlap in time on a device.
  */
 #ifndef FA_H
 #define FA_H
@@ -58,7 +62,9 @@ typedef enum {
                              whose element offsets overflow int64, more
                              than 2^31 rows B*H*N, or (fa_bwd) N*D*4 bytes
                              per head at or above 2^31 */
-  FA_ERR_HIP = 3          /* a HIP runtime call failed (no device, launch error) */
+  FA_ERR_HIP = 3,         /* a HIP runtime call failed (no device, launch error) */
+  FA_ERR_TOO_LARGE = 4    /* fa_bwd_noalloc: the problem needs more scratch than
+                             its static array holds (fa_bwd_noalloc_max_bytes) */
 } fa_status;
 
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -222,6 +228,36 @@ int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o,
               int B, int H, int Nq, int Nk, int D, int causal, float scale,
               int dtype, const fa_bwd_strides* strides, void* workspace,
               size_t workspace_bytes, unsigned stages, hipStream_t stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd_qk (all three stages) with no caller workspace,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * scratch is one static device array of fa_bwd_noalloc_max_bytes() bytes
+ * (64 MiB) per device, which that device holds from the first call on it
+ * until the process ends; the call itself never calls hipMalloc, hipFree or
+ * any allocating routine.  On its first call on a device (the device current
+ * on the calling thread, which must be the stream's device) it looks up the
+ * array's device address once (hipGetSymbolAddress) and keeps it.
+ *   Arguments, layouts, results and errors: as fa_bwd_qk with stages =
+ *   FA_STAGE_ALL, minus the workspace.  A problem whose
+ *   fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D) exceeds
+ *   fa_bwd_noalloc_max_bytes() returns FA_ERR_TOO_LARGE before any HIP call
+ *   (roughly B*H*Nq*(D+1)*4 bytes: B=1 H=8 N=8192 D=128 fits, B=1 H=16
+ *   N=16384 D=64 does not); a failed address lookup returns FA_ERR_HIP.
+ * Every call on one device uses that device's single array.  The kernels
+ * write every scratch value before reading it, so what an earlier call left
+ * there does not matter; but calls that overlap in time on one device
+ * (different streams or host threads) race on it and give wrong results --
+ * serialise them.  dq, dk and dv equal those of fa_bwd_qk bit for bit.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int Nq, int Nk, int D, int causal, float scale,
+                   int dtype, const fa_bwd_strides* strides, hipStream_t stream);
+
+/* Size in bytes of fa_bwd_noalloc's static scratch array (64 MiB). */
+size_t fa_bwd_noalloc_max_bytes(void);
 
 /*
  * fa_merge -- exact combination of P attention results over disjoint key

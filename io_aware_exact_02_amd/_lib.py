@@ -12,14 +12,14 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 FA_F16, FA_BF16 = 0, 1
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split_count", "fa_fwd_fp8", "fa_bwd", "fa_bwd_stages", "fa_bwd_qk",
-           "fa_bwd_workspace_bytes", "fa_bwd_qk_workspace_bytes", "fa_merge", "fa_status_str",
-           "fa_version")
+           "fa_bwd_workspace_bytes", "fa_bwd_qk_workspace_bytes", "fa_bwd_noalloc",
+           "fa_bwd_noalloc_max_bytes", "fa_merge", "fa_status_str", "fa_version")
 STAGE_PREPROCESS, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 
 
@@ -80,6 +80,11 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
                               ctypes.POINTER(BwdStrides), vp, ctypes.c_size_t, ctypes.c_uint, vp]
     lib.fa_bwd_qk.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
+                                   ctypes.POINTER(BwdStrides), vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_max_bytes.argtypes = []
+    lib.fa_bwd_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_kernels.hpp"
 
@@ -151,7 +152,100 @@ SplitWorkspace split_workspace(int B, int H, int Nq, int D, int S) {
 }
 }  // namespace
 
+namespace {
+// Validates the arguments of a backward call (everything but the workspace)
+// and fills the parameter block.
+int make_bwd_params(fa::BwdParams& p, const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                    int H, int Nq, int Nk, int D, int causal, float scale, int dtype,
+                    const fa_bwd_strides* strides) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  int st = check_sizes(B, H, Nq, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  st = check_sizes(B, H, Nk, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  // One head's dQ accumulator is addressed as a buffer of Nq*D*4 bytes.
+  if (static_cast<int64_t>(Nq) * D * 4 > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
+  for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq),
+                          static_cast<const void*>(dk), static_cast<const void*>(dv)}) {
+    if (!aligned16(ptr)) return FA_ERR_UNSUPPORTED;
+  }
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_UNSUPPORTED;
+  p = fa::BwdParams{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  if (strides) {
+    p.sq = from_abi(strides->q);
+    p.sk = from_abi(strides->k);
+    p.sv = from_abi(strides->v);
+    p.so = from_abi(strides->o);
+    p.sdo = from_abi(strides->dout);
+    p.sdq = from_abi(strides->dq);
+    p.sdk = from_abi(strides->dk);
+    p.sdv = from_abi(strides->dv);
+  } else {
+    p.sq = p.so = p.sdo = p.sdq = contiguous(Nq, H, D);
+    p.sk = p.sv = p.sdk = p.sdv = contiguous(Nk, H, D);
+  }
+  for (const fa::Strides* s : {&p.sq, &p.so, &p.sdo, &p.sdq}) {
+    if ((st = check_strides(*s, B, Nq, H, D)) != FA_OK) return st;
+  }
+  for (const fa::Strides* s : {&p.sk, &p.sv, &p.sdk, &p.sdv}) {
+    if ((st = check_strides(*s, B, Nk, H, D)) != FA_OK) return st;
+  }
+  p.B = B;
+  p.H = H;
+  p.N = Nq;
+  p.Nk = Nk;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+// Points the parameter block's scratch at a workspace of at least
+// bwd_workspace(B, H, Nq, Nk, D).total bytes, 256-byte aligned.
+void set_bwd_workspace(fa::BwdParams& p, void* workspace, int B, int H, int Nq, int Nk, int D) {
+  const BwdWorkspace w = bwd_workspace(B, H, Nq, Nk, D);
+  char* ws = static_cast<char*>(workspace);
+  p.dvec = reinterpret_cast<float*>(ws + w.dvec);
+  p.dq_fix = reinterpret_cast<int32_t*>(ws + w.dq);
+  p.bound_part = reinterpret_cast<float*>(ws + w.part);
+  p.dq_bound = reinterpret_cast<float*>(ws + w.unit);
+}
+
+// Scratch of fa_bwd_noalloc: one static device array.  In host code its name
+// stands for a host-side shadow, so kernels get its device address, looked
+// up once per device (with that device current) and kept.
+constexpr size_t kNoallocScratchBytes = size_t{64} << 20;
+__device__ __align__(256) unsigned char fa_noalloc_scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(fa_noalloc_scratch)) != hipSuccess || !ptr)
+      return FA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+}  // namespace
+
 extern "C" {
+
 
 int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int Nq, int Nk, int D, int causal, float scale, int dtype,
@@ -307,63 +401,33 @@ int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const 
               int D, int causal, float scale, int dtype, const fa_bwd_strides* strides,
               void* workspace, size_t workspace_bytes, unsigned stages, hipStream_t stream) {
   if (stages == 0 || (stages & ~FA_STAGE_ALL) != 0) return FA_ERR_INVALID_ARG;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID_ARG;
-  int st = check_sizes(B, H, Nq, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  st = check_sizes(B, H, Nk, D, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  // One head's dQ accumulator is addressed as a buffer of Nq*D*4 bytes.
-  if (static_cast<int64_t>(Nq) * D * 4 > (int64_t{1} << 31) - 1) return FA_ERR_UNSUPPORTED;
-  if (workspace_bytes < fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D)) return FA_ERR_INVALID_ARG;
-  for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq),
-                          static_cast<const void*>(dk), static_cast<const void*>(dv)}) {
-    if (!aligned16(ptr)) return FA_ERR_UNSUPPORTED;
-  }
-  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_UNSUPPORTED;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_UNSUPPORTED;
+  if (!workspace) return FA_ERR_INVALID_ARG;
   fa::BwdParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<const uint16_t*>(o);
-  p.dout = static_cast<const uint16_t*>(dout);
-  p.lse = lse;
-  p.dq = static_cast<uint16_t*>(dq);
-  p.dk = static_cast<uint16_t*>(dk);
-  p.dv = static_cast<uint16_t*>(dv);
-  if (strides) {
-    p.sq = from_abi(strides->q);
-    p.sk = from_abi(strides->k);
-    p.sv = from_abi(strides->v);
-    p.so = from_abi(strides->o);
-    p.sdo = from_abi(strides->dout);
-    p.sdq = from_abi(strides->dq);
-    p.sdk = from_abi(strides->dk);
-    p.sdv = from_abi(strides->dv);
-  } else {
-    p.sq = p.so = p.sdo = p.sdq = contiguous(Nq, H, D);
-    p.sk = p.sv = p.sdk = p.sdv = contiguous(Nk, H, D);
-  }
-  for (const fa::Strides* s : {&p.sq, &p.so, &p.sdo, &p.sdq}) {
-    if ((st = check_strides(*s, B, Nq, H, D)) != FA_OK) return st;
-  }
-  for (const fa::Strides* s : {&p.sk, &p.sv, &p.sdk, &p.sdv}) {
-    if ((st = check_strides(*s, B, Nk, H, D)) != FA_OK) return st;
-  }
-  const BwdWorkspace w = bwd_workspace(B, H, Nq, Nk, D);
-  char* ws = static_cast<char*>(workspace);
-  p.dvec = reinterpret_cast<float*>(ws + w.dvec);
-  p.dq_fix = reinterpret_cast<int32_t*>(ws + w.dq);
-  p.bound_part = reinterpret_cast<float*>(ws + w.part);
-  p.dq_bound = reinterpret_cast<float*>(ws + w.unit);
-  p.B = B;
-  p.H = H;
-  p.N = Nq;
-  p.Nk = Nk;
-  p.scale = scale;
-  p.c = scale * 1.4426950408889634f;
+  int st = make_bwd_params(p, q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, causal, scale,
+                           dtype, strides);
+  if (st != FA_OK) return st;
+  if (workspace_bytes < fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D)) return FA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_UNSUPPORTED;
+  set_bwd_workspace(p, workspace, B, H, Nq, Nk, D);
   const hipError_t e = fa::launch_bwd(p, dtype, D, causal, stages, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                   int H, int Nq, int Nk, int D, int causal, float scale, int dtype,
+                   const fa_bwd_strides* strides, hipStream_t stream) {
+  fa::BwdParams p{};
+  int st = make_bwd_params(p, q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, causal, scale,
+                           dtype, strides);
+  if (st != FA_OK) return st;
+  if (fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D) > kNoallocScratchBytes) return FA_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  if ((st = noalloc_scratch(&scratch)) != FA_OK) return st;
+  set_bwd_workspace(p, scratch, B, H, Nq, Nk, D);
+  const hipError_t e = fa::launch_bwd(p, dtype, D, causal, FA_STAGE_ALL, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -413,6 +477,8 @@ const char* fa_status_str(int status) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head dim, alignment or stride";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: problem needs more scratch than fa_bwd_noalloc's static array";
     default: return "unknown fa status";
   }
 }

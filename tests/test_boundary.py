@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_status_strings():
     lib = _lib.load()
     assert lib.fa_version().decode().startswith("fa-gfx950")
-    for st in range(4):
+    for st in range(5):
         assert lib.fa_status_str(st)
     assert b"unknown" in lib.fa_status_str(99)
 
@@ -333,3 +333,32 @@ def test_huge_sizes_do_not_overflow():
                          None) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_merge(P, P, big, P, P, 1 << 15, 1 << 15, 1, 64, _lib.FA_BF16,
                         None) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_before_launch():
+    """fa_bwd_noalloc validates like fa_bwd_qk, and a problem whose backward
+    scratch exceeds the static array's size is refused with FA_ERR_TOO_LARGE,
+    all before any HIP call (none is made here: no device is needed)."""
+    lib = _lib.load()
+    cap = int(lib.fa_bwd_noalloc_max_bytes())
+    assert cap == 64 << 20
+
+    def call(ptrs=None, B=1, H=1, Nq=128, Nk=128, D=64, causal=0, scale=0.125,
+             dtype=_lib.FA_BF16, strides=None):
+        ptrs = [P] * 9 if ptrs is None else ptrs
+        return lib.fa_bwd_noalloc(*ptrs, B, H, Nq, Nk, D, causal, scale, dtype, strides, None)
+
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == _lib.FA_ERR_INVALID_ARG, i
+    assert call(D=80) == _lib.FA_ERR_UNSUPPORTED
+    assert call(causal=2) == _lib.FA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == _lib.FA_ERR_INVALID_ARG
+    assert call(B=0) == _lib.FA_ERR_INVALID_ARG
+    # Largest N whose scratch fits, and the next size up.
+    fits = [n for n in (8192, 16384) if lib.fa_bwd_qk_workspace_bytes(1, 8, n, n, 128) <= cap]
+    assert fits == [8192]
+    assert call(B=1, H=16, Nq=16384, Nk=16384, D=64, causal=1) == _lib.FA_ERR_TOO_LARGE
+    assert call(B=1, H=8, Nq=16384, Nk=16384, D=128) == _lib.FA_ERR_TOO_LARGE
+    assert b"TOO_LARGE" in lib.fa_status_str(_lib.FA_ERR_TOO_LARGE)
