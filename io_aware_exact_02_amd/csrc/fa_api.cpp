@@ -63,20 +63,27 @@ size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
 namespace {
 // Workspace layout of the backward, each part starting on a 256-byte
 // boundary: Dvec [B, H, Nq] fp32 | dQ accumulator [B, H, Nq, D] int32 |
-// bound maxima [B*H, 3, ceil(max(Nq, Nk) / 16)] fp32 | dQ bound [B*H] fp32.
+// bound maxima [B*H, 3, ceil(max(Nq, Nk) / 16)] fp32 | dQ bound [B*H] fp32 |
+// partial dK and dV sums [S, B*H, Nk, D] fp32 each, S the query segments of
+// a causal launch of this size (none when S = 1; sized for causal, so that
+// the size does not depend on the mask).
 struct BwdWorkspace {
-  size_t dvec, dq, part, unit, total;
+  size_t dvec, dq, part, unit, dk_part, dv_part, total;
 };
 BwdWorkspace bwd_workspace(int B, int H, int Nq, int Nk, int D) {
   const size_t heads = static_cast<size_t>(B) * H;
   const size_t rows = heads * Nq;
   const size_t nmax = static_cast<size_t>(Nq > Nk ? Nq : Nk);
+  const int segs = fa::bwd_segments(B, H, Nk, D, true);
+  const size_t part_bytes = segs > 1 ? static_cast<size_t>(segs) * heads * Nk * D * sizeof(float) : 0;
   BwdWorkspace w{};
   w.dvec = 0;
   w.dq = align256(rows * sizeof(float));
   w.part = w.dq + align256(rows * D * sizeof(int32_t));
   w.unit = w.part + align256(heads * 3 * ((nmax + 15) / 16) * sizeof(float));
-  w.total = w.unit + align256(heads * sizeof(float));
+  w.dk_part = w.unit + align256(heads * sizeof(float));
+  w.dv_part = w.dk_part + align256(part_bytes);
+  w.total = w.dv_part + align256(part_bytes);
   return w;
 }
 }  // namespace
@@ -218,6 +225,8 @@ void set_bwd_workspace(fa::BwdParams& p, void* workspace, int B, int H, int Nq, 
   p.dq_fix = reinterpret_cast<int32_t*>(ws + w.dq);
   p.bound_part = reinterpret_cast<float*>(ws + w.part);
   p.dq_bound = reinterpret_cast<float*>(ws + w.unit);
+  p.dk_part = reinterpret_cast<float*>(ws + w.dk_part);
+  p.dv_part = reinterpret_cast<float*>(ws + w.dv_part);
 }
 
 // Scratch of fa_bwd_noalloc: one static device array.  In host code its name

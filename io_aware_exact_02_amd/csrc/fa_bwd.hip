@@ -17,6 +17,9 @@
 //      query tiles; dQ contributions are added to the accumulator with
 //      integer atomics (fixed point, see below);
 //   3. dQ conversion: scale, round to the input type, strided store.
+// Causal launches with few key blocks split each key block's query tiles
+// over two workgroups (query segments); a small kernel then adds their fp32
+// partial dK, dV sums in a fixed order.
 //
 // dQ accumulator.  Each dQ element receives one partial sum per key block,
 // from different workgroups, so the sum needs device-wide atomics; on this
@@ -115,11 +118,18 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 // writes dS^T to LDS, and after the tile barrier the waves compute
 //   dQ(tile) = dS K                   (A: dS, B: K, both gathered transposed)
 // one 32x32 output block per wave over all BKV keys, so each dQ element
-// receives one fp32 atomic per workgroup.  The atomics of a tile are issued
-// in the next iteration, after that iteration's prefetch loads, so that no
-// load ever waits behind them.  Q, dO, LSE and Dvec of the next tile are
-// prefetched into registers during the current one (LDS double buffer, one
-// barrier per tile).
+// receives one 32-bit fixed-point integer atomic (units of B / 2^30) per
+// workgroup.  The atomics of a tile are issued in the next iteration, after
+// that iteration's prefetch loads, so that no load ever waits behind them.
+// Q, dO, LSE and Dvec of the next tile are prefetched into registers during
+// the current one (LDS double buffer, one barrier per tile).
+//
+// Query segments (SEG, BwdParams nseg > 1): the query tiles of each key
+// block are cut into nseg contiguous segments, each run by its own
+// workgroup, which writes fp32 partial dK, dV sums to the workspace instead
+// of dk, dv; bwd_dkdv_merge_kernel adds the nseg partials in segment order.
+// This evens out causal launches with few key blocks, where the first key
+// block's query range is the whole sequence and the last one's one tile.
 template <int D, int NW, int BQ_>
 struct BwdCfg {
   static constexpr int BKV = 32 * NW;   // keys per workgroup
@@ -134,7 +144,7 @@ struct BwdCfg {
   static_assert(QPT * THREADS == BQ * CPR, "tile load must divide evenly");
 };
 
-template <typename T, int D, int NW, int BQ_, bool KLDS, bool CAUSAL>
+template <typename T, int D, int NW, int BQ_, bool KLDS, bool CAUSAL, bool SEG>
 __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   using Cfg = BwdCfg<D, NW, BQ_>;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NQB = Cfg::NQB, DB = Cfg::DB;
@@ -159,7 +169,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 
   const int BH = p.B * p.H;
   const int bh = blockIdx.x % BH;
-  const int kblk = static_cast<int>(blockIdx.x / BH);
+  // blockIdx.x = (kblk * nseg + seg) * BH + bh: heaviest key blocks first.
+  const int item = static_cast<int>(blockIdx.x / BH);
+  const int kblk = SEG ? item / p.nseg : item;
+  const int seg = SEG ? item % p.nseg : 0;
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;    // query rows
@@ -226,11 +239,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       m1 = fmaxf(m1, red[w][1]);
       m2 = fmaxf(m2, red[w][2]);
     }
-    // A non-finite bound (non-finite inputs) gives dQ = 0.
+    // A non-finite bound (non-finite inputs) adds zeros to the accumulator
+    // and records a NaN bound, so that the conversion returns NaN for dq.
     const float bound = fmaxf((4.0f * D) * m0 * m1 * m2, 0x1p-96f);
     const bool usable = bound < INFINITY;
     dq_scale = usable ? 0x1p30f / bound : 0.0f;
-    if (kblk == 0 && tid == 0) p.dq_bound[bh] = usable ? bound : 0.0f;
+    if (item == 0 && tid == 0) p.dq_bound[bh] = usable ? bound : __builtin_nanf("");
   }
 
   // The workgroup's K rows in LDS (B operand of dQ = dS K).
@@ -276,10 +290,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   // ---- next-tile staging: global pointers, LDS offsets, registers
-  // Causal: the first query that sees the workgroup's first key (the last
-  // query sees every key, so at least one tile remains).
-  const int q_begin = CAUSAL ? max(kb0 - off, 0) : 0;
-  const int ntiles = (N - q_begin + BQ - 1) / BQ;
+  // Causal: from the first query that sees the workgroup's first key (the
+  // last query sees every key, so at least one tile remains).  With query
+  // segments, this workgroup takes segment seg of those tiles (possibly
+  // none).
+  const int q_first = CAUSAL ? max(kb0 - off, 0) : 0;
+  const int tiles_all = (N - q_first + BQ - 1) / BQ;
+  const int nseg = SEG ? p.nseg : 1;
+  const int seg_len = (tiles_all + nseg - 1) / nseg;
+  const int t_lo = min(seg * seg_len, tiles_all);
+  const int ntiles = min(tiles_all - t_lo, seg_len);
+  const int q_begin = q_first + t_lo * BQ;
   const uint16_t* qptr[QPT];
   const uint16_t* doptr[QPT];
   int ld_row[QPT];
@@ -486,8 +507,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  load_tile(0);
-  store_tile(IntC<0>{});
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(IntC<0>{});
+  }
   __syncthreads();
   for (int t = 0; t < ntiles; t += 2) {
     step(IntC<0>{}, t);
@@ -496,18 +519,35 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   if (ntiles > 0) dq_atomics(q_begin + (ntiles - 1) * BQ);
 
   // Epilogue: dK = scale * sum dS^T Q, dV = sum P^T dO.  C value i: key
-  // kw0 + c_row(i, hh), d = 32*db + l32.
+  // kw0 + c_row(i, hh), d = 32*db + l32.  With query segments, the unscaled
+  // fp32 sums go to the workspace: partial sums [seg][bh][key][d].
+  if constexpr (!SEG) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk = kw0 + c_row(i, hh);
-      if (kk < Nk) {
-        const int d = 32 * db + l32;
-        p.dk[b * p.sdk.b + static_cast<int64_t>(kk) * p.sdk.n + h * p.sdk.h + d] =
-            to_half_bits<T>(dkacc[db][i] * p.scale);
-        p.dv[b * p.sdv.b + static_cast<int64_t>(kk) * p.sdv.n + h * p.sdv.h + d] =
-            to_half_bits<T>(dvacc[db][i]);
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kw0 + c_row(i, hh);
+        if (kk < Nk) {
+          const int d = 32 * db + l32;
+          p.dk[b * p.sdk.b + static_cast<int64_t>(kk) * p.sdk.n + h * p.sdk.h + d] =
+              to_half_bits<T>(dkacc[db][i] * p.scale);
+          p.dv[b * p.sdv.b + static_cast<int64_t>(kk) * p.sdv.n + h * p.sdv.h + d] =
+              to_half_bits<T>(dvacc[db][i]);
+        }
+      }
+    }
+  } else {
+    const int64_t base = (static_cast<int64_t>(seg) * BH + bh) * Nk;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = kw0 + c_row(i, hh);
+        if (kk < Nk) {
+          const int64_t e = (base + kk) * D + 32 * db + l32;
+          p.dk_part[e] = dkacc[db][i];
+          p.dv_part[e] = dvacc[db][i];
+        }
       }
     }
   }
@@ -522,7 +562,58 @@ struct BwdShape {
   static constexpr int NW = D == 64 ? 8 : 4;
   static constexpr int BQ = 64;
   static constexpr bool KLDS = false;
+  static constexpr int BKV = BwdCfg<D, NW, BQ>::BKV;
 };
+
+// Query segments per key block (BwdParams nseg): 2 for causal launches with
+// fewer than two key blocks per compute unit (256 on MI355X), where the
+// heaviest key block holds about twice the average work; 1 otherwise.
+// (One GPU's share of B1 H16 N16384 D64 under 8-way head sharding, 128 key
+// blocks: forward + backward 0.73 -> 0.49 ms.)
+int bwd_segments(int B, int H, int Nk, int D, bool causal) {
+  const int bkv = D == 64 ? BwdShape<64>::BKV : BwdShape<128>::BKV;
+  const int64_t blocks = static_cast<int64_t>(B) * H * ((Nk + bkv - 1) / bkv);
+  return causal && blocks < 2 * 256 ? 2 : 1;
+}
+
+// ------------------------------------------------------------------ kernel 2b
+// Sum of the nseg fp32 partial dK, dV of a segmented launch, in segment
+// order (deterministic), scaled (dK), rounded and stored.  Grid
+// (ceil(Nk / RPB), B*H).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_merge_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int tid = threadIdx.x;
+  const int part = tid % TPR;
+  const int bh = blockIdx.y;
+  const int n = static_cast<int>(blockIdx.x) * RPB + tid / TPR;
+  if (n >= p.Nk) return;
+  const int b = bh / p.H, h = bh % p.H;
+  const int BH = p.B * p.H;
+  float k8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float v8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sgi = 0; sgi < p.nseg; ++sgi) {
+    const int64_t e = ((static_cast<int64_t>(sgi) * BH + bh) * p.Nk + n) * D + part * 8;
+    const f32x4 ka = *reinterpret_cast<const f32x4*>(p.dk_part + e);
+    const f32x4 kb = *reinterpret_cast<const f32x4*>(p.dk_part + e + 4);
+    const f32x4 va = *reinterpret_cast<const f32x4*>(p.dv_part + e);
+    const f32x4 vb = *reinterpret_cast<const f32x4*>(p.dv_part + e + 4);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      k8[x] += ka[x];
+      k8[x + 4] += kb[x];
+      v8[x] += va[x];
+      v8[x + 4] += vb[x];
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) k8[x] *= p.scale;
+  stg16(p.dk + b * p.sdk.b + static_cast<int64_t>(n) * p.sdk.n + h * p.sdk.h + part * 8,
+        pack8<T>(k8));
+  stg16(p.dv + b * p.sdv.b + static_cast<int64_t>(n) * p.sdv.n + h * p.sdv.h + part * 8,
+        pack8<T>(v8));
+}
 
 // ------------------------------------------------------------------ kernel 3
 // Grid (ceil(N / RPB), B*H): dq = scale * B * (accumulator / 2^30).
@@ -555,7 +646,8 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   using Sh = BwdShape<D>;
   constexpr int NW = Sh::NW;
   BwdParams p = p_in;
-  p.num_kblocks = (p.Nk + BwdCfg<D, NW, Sh::BQ>::BKV - 1) / BwdCfg<D, NW, Sh::BQ>::BKV;
+  p.num_kblocks = (p.Nk + Sh::BKV - 1) / Sh::BKV;
+  p.nseg = bwd_segments(p.B, p.H, p.Nk, D, CAUSAL);
   constexpr int RPB = 256 / (D / 8);
   p.npart = (max(p.N, p.Nk) + RPB - 1) / RPB;
   const dim3 row_grid(static_cast<unsigned>(p.npart), static_cast<unsigned>(p.B * p.H));
@@ -565,10 +657,21 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2u) {
-    const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL>),
-                       dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
+    const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks * p.nseg;
+    if (CAUSAL && p.nseg > 1) {  // only causal launches use query segments
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, CAUSAL>),
+                         dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, false>),
+                         dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.nseg > 1) {
+      const dim3 key_grid(static_cast<unsigned>((p.Nk + RPB - 1) / RPB),
+                          static_cast<unsigned>(p.B * p.H));
+      hipLaunchKernelGGL((bwd_dkdv_merge_kernel<T, D>), key_grid, dim3(256), 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if (stages & 4u) {
     hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, s, p);

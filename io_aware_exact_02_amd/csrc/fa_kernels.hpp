@@ -64,10 +64,13 @@ struct BwdParams {
   int32_t* dq_fix;    // workspace: [B, H, N, D] dQ accumulator, fixed point
   float* bound_part;  // workspace: [B*H, 3, npart] maxima per row block
   float* dq_bound;    // workspace: [B*H] dQ bound B; one fixed-point unit = B / 2^30
+  float* dk_part;     // workspace: [nseg, B*H, Nk, D] partial dK sums (nseg > 1)
+  float* dv_part;     // workspace: [nseg, B*H, Nk, D] partial dV sums (nseg > 1)
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, N;      // N: query rows
   int Nk;           // keys (causal: query i sees keys j <= i + Nk - N)
   int num_kblocks;  // ceil(Nk / keys per workgroup)
+  int nseg;         // query segments per key block (set by the launcher)
   int npart;        // row blocks per head in bound_part
   float scale;
   float c;  // scale * log2(e)
@@ -100,6 +103,9 @@ hipError_t launch_fwd64(const FwdParams& p, int dtype, bool causal, hipStream_t 
 // stages: bit 0 preprocess, bit 1 dK/dV (+ dQ accumulation), bit 2 dQ conversion.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
                       hipStream_t s);
+// Query segments per key block of the dK/dV kernel for a launch (1 or 2);
+// the backward workspace holds partial dK, dV sums for that many.
+int bwd_segments(int B, int H, int Nk, int D, bool causal);
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_split_merge(const SplitMergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_fwd8(const Fwd8Params& p, int out_dtype, int D, int causal, hipStream_t s);
