@@ -155,9 +155,11 @@ int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
  * fa_bwd_workspace_bytes -- size of the scratch fa_bwd needs: the row vector
  * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
  * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]
- * (fp32) and one dQ bound per head [B*H] (fp32), each part rounded
- * up to 256 bytes.  O(N*D) per head; no N*N term.  Returns 0 for invalid
- * sizes.
+ * (fp32), one dQ bound per head [B*H] (fp32), and -- for launches with fewer than 512
+ * key blocks of 256 (D = 64) or 128 (D = 128) keys, which a causal mask
+ * splits into two query segments -- partial dK and dV sums [2, B, H, N, D]
+ * (fp32) each; every part rounded up to 256 bytes.  O(N*D) per head; no N*N
+ * term.  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 
@@ -178,14 +180,16 @@ size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
  *                     fa_bwd_workspace_bytes(B, H, N, D) bytes, 256-byte
  *                     aligned; contents undefined on entry and on exit.
  * Three kernels are enqueued on `stream`: the Dvec preprocess (which also
- * clears the dQ accumulator and takes the largest |dO|, |K| and |V|
- * elements per head), the K/V-block-parallel dK/dV kernel that accumulates
- * dQ with 32-bit integer atomics in units of B / 2^30, B = 4 D max|dO|
- * max|K| max|V| per (batch, head) -- a bound on any partial sum of dS K
- * -- and the dQ conversion.  The integer sum is exact, so dq is bitwise
- * reproducible; each key block's contribution is rounded to the nearest
- * unit.  B is raised to at least 2^-96 (the scale 2^30 / B stays finite);
- * heads whose bound is not finite (non-finite inputs) get dq = 0.
+ * clears the dQ accumulator and takes the largest |dO_i|, |K| element
+ * and |V_j| per head, |.| the Euclidean norm of a row), the K/V-block-
+ * parallel dK/dV kernel that accumulates dQ with 32-bit integer atomics in
+ * units of B / 2^30, B = 4 max|K| max|dO_i| max|V_j| per (batch, head) --
+ * a bound on any partial sum of dS K -- and the dQ conversion (narrow
+ * causal launches add a fourth, which sums the partial dK, dV of the query
+ * segments).  The integer sum is exact, so dq is bitwise reproducible;
+ * each key block's contribution is rounded to the nearest unit.  B is
+ * raised to at least 2^-96 (the scale 2^30 / B stays finite); heads whose
+ * bound is not finite (non-finite inputs) get dq = NaN.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse, void* dq, void* dk, void* dv,

@@ -25,26 +25,63 @@
 // from different workgroups, so the sum needs device-wide atomics; on this
 // chip those execute at the memory side and bound the whole backward.
 // 32-bit integer adds run there about 1.3x faster than fp32 adds, so the
-// accumulator is fixed point: one unit is B / 2^30, with B a bound on
-// |sum_j dS_ij K_jd| over any subset of keys.  From dS_ij = P_ij (dP_ij -
-// Dvec_i), sum_j P_ij = 1, |dP_ij| = |dO_i . V_j| <= D max|dO| max|V| and
-// |Dvec_i| = |dO_i . O_i| <= D max|dO| max|V| (O_i is a convex combination
-// of the V_j), with element-wise maxima over the head:
-//   B = 4 D max|dO| max|K| max|V|   (2x margin for rounding),
-// per (batch, head).  Element-wise maxima, not norms: squares of tiny or
-// huge inputs would under- or overflow.  Every partial sum is rounded to the nearest unit; the
-// total stays within 2^30 units, so the 32-bit sum is exact whatever the
-// order of the adds -- dQ is deterministic -- and its error is at most half
-// a unit per key block (rounding half up, v_cvt_rpi_i32_f32).
+// accumulator is fixed point: one unit is B / 2^30 per (batch, head), with
+// B a bound on |sum_j dS_ij K_jd| over any subset of keys:
+//   |dP_ij| = |dO_i . V_j| <= |dO_i| |V_j|  and  |Dvec_i| = |dO_i . O_i| <=
+//   |dO_i| max_j |V_j|  (O_i is a convex combination of the V_j; |.| the
+//   Euclidean norm), so |dS_ij| <= 2 P_ij |dO_i| max_j |V_j|, and with
+//   sum_j P_ij = 1:
+//   B = 4 max_jd |K_jd| max_i |dO_i| max_j |V_j|    (2x margin for rounding),
+// maxima over the head.  The norms are computed with the row maximum
+// factored out, so squares of tiny or huge inputs cannot under- or
+// overflow.  (Row norms instead of element maxima: |dO_i| |V_j| is at most
+// D max|dO| max|V|, and for typical data about D/8 times smaller.)  Every
+// partial sum is rounded to the nearest unit; the total stays within 2^30
+// units, so the 32-bit sum is exact whatever the order of the adds -- dQ is
+// deterministic -- and its error is at most half a unit per key block
+// (rounding half up, v_cvt_rpi_i32_f32).  A non-finite bound (non-finite
+// inputs) gives dq = NaN.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 
 // ------------------------------------------------------------------ kernel 1
+// Norm of a row of D halves held as TPR consecutive lanes of 8 halves each
+// (a: this lane's 8), computed with the row maximum factored out so that the
+// squares neither under- nor overflow; +inf when any element is not finite.
+template <typename T, int TPR>
+__device__ __forceinline__ float row_norm(const u32x4& a) {
+  float m = absmax8<T>(a);
+  float z = 0.0f;  // NaN when an element is inf or NaN
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    z += half_bits_to_float<T>(a[w] & 0xffffu) * 0.0f;
+    z += half_bits_to_float<T>(a[w] >> 16) * 0.0f;
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o, 64));
+    z += __shfl_xor(z, o, 64);
+  }
+  const float inv = m > 0.0f ? 1.0f / m : 0.0f;
+  float ss = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x0 = half_bits_to_float<T>(a[w] & 0xffffu) * inv;
+    const float x1 = half_bits_to_float<T>(a[w] >> 16) * inv;
+    ss = fmaf(x0, x0, ss);
+    ss = fmaf(x1, x1, ss);
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  return z == 0.0f ? m * __builtin_sqrtf(ss) : INFINITY;
+}
+
 // Grid (ceil(max(N, Nk) / RPB), B*H): each workgroup covers RPB query and
-// key rows of one head and records the largest |dO|, |K| and |V| elements of
-// those rows.
+// key rows of one head.  Per query row: Dvec = rowsum(dO o O) and a cleared
+// dQ accumulator row; per workgroup, the largest |dO_i|, |K| element and
+// |V_j| of its rows (+inf for non-finite inputs).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   constexpr int TPR = D / 8;       // threads per row (8 elements each)
@@ -55,13 +92,15 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   const int b = bh / p.H, h = bh % p.H;
   const int n = static_cast<int>(blockIdx.x) * RPB + tid / TPR;
   const int64_t row = static_cast<int64_t>(bh) * p.N + n;
-  float s = 0.0f, domax = 0.0f, vmax = 0.0f, kmax = 0.0f;
+  float s = 0.0f, donorm = 0.0f, vnorm = 0.0f, kmax = 0.0f;
   const int64_t nn = n;
+  // The TPR lanes of a row are consecutive and take the same branches, so
+  // the row reductions (shuffles within the row) see only active lanes.
   if (n < p.N) {  // query row n
     const u32x4 o = ldg16(p.o + b * p.so.b + nn * p.so.n + h * p.so.h + part * 8);
     const u32x4 d = ldg16(p.dout + b * p.sdo.b + nn * p.sdo.n + h * p.sdo.h + part * 8);
     s = dot8<T>(o, d);
-    domax = absmax8<T>(d);
+    donorm = row_norm<T, TPR>(d);
     int32_t* acc = p.dq_fix + row * D + part * 8;
     const u32x4 z = {0u, 0u, 0u, 0u};
     stg16(acc, z);
@@ -70,8 +109,14 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   if (n < p.Nk) {  // key row n
     const u32x4 k = ldg16(p.k + b * p.sk.b + nn * p.sk.n + h * p.sk.h + part * 8);
     const u32x4 v = ldg16(p.v + b * p.sv.b + nn * p.sv.n + h * p.sv.h + part * 8);
-    vmax = absmax8<T>(v);
-    kmax = absmax8<T>(k);
+    vnorm = row_norm<T, TPR>(v);
+    float z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      z += half_bits_to_float<T>(k[w] & 0xffffu) * 0.0f;
+      z += half_bits_to_float<T>(k[w] >> 16) * 0.0f;
+    }
+    kmax = z == 0.0f ? absmax8<T>(k) : INFINITY;
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
@@ -79,15 +124,15 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
   // Maxima over the workgroup's rows: across the wave, then the four waves.
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    domax = fmaxf(domax, __shfl_xor(domax, off, 64));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    donorm = fmaxf(donorm, __shfl_xor(donorm, off, 64));
+    vnorm = fmaxf(vnorm, __shfl_xor(vnorm, off, 64));
     kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
   }
   __shared__ float red[4][3];
   if ((tid & 63) == 0) {
-    red[tid >> 6][0] = domax;
+    red[tid >> 6][0] = donorm;
     red[tid >> 6][1] = kmax;
-    red[tid >> 6][2] = vmax;
+    red[tid >> 6][2] = vnorm;
   }
   __syncthreads();
   if (tid == 0) {
@@ -207,7 +252,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     vreg[kc] = vv;
   }
   // Fixed-point scale of the dQ accumulator for this head (see the file
-  // comment), from the preprocess maxima: x -> round(x * 2^30 / B).  B is
+  // comment), from the preprocess maxima of |dO_i|, |K| and |V_j|:
+  // x -> round(x * 2^30 / B).  B is
   // raised to at least 2^-96 so that the scale stays finite; a larger B is
   // still a bound, and gradients that small keep an absolute resolution of
   // 2^-126.  Workgroup 0 of the head records B for the conversion.
@@ -239,9 +285,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       m1 = fmaxf(m1, red[w][1]);
       m2 = fmaxf(m2, red[w][2]);
     }
-    // A non-finite bound (non-finite inputs) adds zeros to the accumulator
-    // and records a NaN bound, so that the conversion returns NaN for dq.
-    const float bound = fmaxf((4.0f * D) * m0 * m1 * m2, 0x1p-96f);
+    // B = 4 max|dO_i| max|K| max|V_j| (norms, see the file comment).  A
+    // non-finite bound (non-finite inputs) adds zeros to the accumulator and
+    // records a NaN bound, so that the conversion returns NaN for dq.
+    const float bound = fmaxf(4.0f * m0 * m1 * m2, 0x1p-96f);
     const bool usable = bound < INFINITY;
     dq_scale = usable ? 0x1p30f / bound : 0.0f;
     if (item == 0 && tid == 0) p.dq_bound[bh] = usable ? bound : __builtin_nanf("");

@@ -50,7 +50,7 @@ def test_workspace_bytes_is_linear_in_n():
         return (x + 255) // 256 * 256
 
     # Dvec, the int32 dQ accumulator, three maxima per 16-row block, one
-    # fixed-point unit per head, and -- for launches with fewer than 512 key
+    # fixed-point bound per head, and -- for launches with fewer than 512 key
     # blocks (256 keys at head_dim 64, 128 at head_dim 128), which a causal
     # mask splits into two query segments -- two fp32 partial dK and dV
     # sums: O(N*D) per head, no N*N term.
@@ -59,8 +59,8 @@ def test_workspace_bytes_is_linear_in_n():
         bkv = 256 if D == 64 else 128
         segs = 2 if heads * ((N + bkv - 1) // bkv) < 512 else 1
         part = 2 * a256(4 * segs * heads * N * D) if segs > 1 else 0
-        return (a256(4 * rows) + a256(4 * rows * D) + a256(4 * 3 * heads * ((N + 15) // 16))
-                + a256(4 * heads) + part)
+        return (a256(4 * rows) + a256(4 * rows * D)
+                + a256(4 * 3 * heads * ((N + 15) // 16)) + a256(4 * heads) + part)
 
     for (B, H, N, D) in [(1, 1, 1, 64), (2, 12, 2048, 64), (1, 16, 16384, 64), (1, 8, 8192, 128),
                          (3, 5, 1000, 128), (1, 2, 16384, 64)]:
@@ -187,8 +187,8 @@ def test_unequal_length_entry_points_reject_before_launch():
     need = lib.fa_bwd_qk_workspace_bytes(1, 1, 128, 256, 64)
     a256 = lambda x: (x + 255) // 256 * 256
     # one key block: the partial dK, dV sums of two query segments over Nk keys
-    assert need == (a256(4 * 128) + a256(4 * 128 * 64) + a256(4 * 3 * (256 // 16)) + a256(4)
-                    + 2 * a256(4 * 2 * 256 * 64))
+    assert need == (a256(4 * 128) + a256(4 * 128 * 64) + a256(4 * 3 * (256 // 16))
+                    + a256(4) + 2 * a256(4 * 2 * 256 * 64))
     assert lib.fa_bwd_qk_workspace_bytes(1, 1, 0, 256, 64) == 0
     assert lib.fa_bwd_qk_workspace_bytes(1, 1, 5, 5, 64) == lib.fa_bwd_workspace_bytes(1, 1, 5, 64)
 
