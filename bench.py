@@ -18,12 +18,17 @@ two), both halved for causal masking.
 Prints ONE JSON line.  Besides the headline value it carries
   roofline     : the dominant kernel (the dK/dV backward kernel at c5) timed
                  with HIP events on its own stream inside the timed region,
-                 against the 2516.6 TFLOP/s dense MFMA peak;
+                 against the 2516.6 TFLOP/s dense MFMA peak, with what limits
+                 it in this run (its dQ atomics against their memory-side
+                 rate, else the matrix cores);
+  clock        : the gfx clock sampled with amdsmi while further untimed
+                 steps of the same sweep run, and the MFMA peak at it;
   cpu_baseline : the fp64 CPU oracle timed on a bounded sample (c5 heads);
   dq_atomics   : the same kernel's 32-bit dQ accumulator atomics per launch
                  and their achieved rate over its launch time (these adds
                  execute at the memory side and bound the backward);
-  per_config   : forward / backward times and TFLOP/s per workload;
+  per_config   : forward / backward times (mean, median, min over the timed
+                 steps) and TFLOP/s per workload;
   memory_c3    : peak device memory of fused fwd+bwd vs an unfused S/P
                  PyTorch baseline at c3 (untimed pass);
   pages_sweep  : the pages' own forward speed comparison (standard fp16
@@ -48,7 +53,9 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -436,6 +443,68 @@ def mha_layer(torch, fa):
             "max_output_diff": diff}
 
 
+# Memory-side rate of 32-bit integer atomics measured with a throughput probe
+# on MI355X (any address pattern): the ceiling of the dQ accumulation.
+DQ_ATOMIC_PROBE_G_PER_S = 412.0
+
+
+def gfx_clock_sampler():
+    """A start/stop pair that samples the GPU's gfx clock (MHz) through
+    amdsmi in a background thread, or None when amdsmi is unavailable."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+                v = m.get(key)
+                if isinstance(v, (list, tuple)):
+                    v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+                    if v:
+                        return float(statistics.mean(v))
+                elif isinstance(v, (int, float)) and 0 < v < 10000:
+                    return float(v)
+        except Exception:
+            pass
+        try:
+            info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+            v = info.get("clk")
+            return float(v) if isinstance(v, (int, float)) and v > 0 else None
+        except Exception:
+            return None
+
+    samples = []
+    stop = threading.Event()
+
+    def loop():
+        while not stop.is_set():
+            v = read()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.005)
+
+    th = threading.Thread(target=loop, daemon=True)
+
+    def start():
+        th.start()
+
+    def finish():
+        stop.set()
+        th.join(timeout=2)
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        return samples
+
+    return start, finish
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,6 +525,9 @@ def main(argv=None):
                     help="skip the key-split forward measurement")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the one-GPU share of c5 under 8-way head sharding")
+    ap.add_argument("--clock-seconds", type=float, default=1.0,
+                    help="after timing, run untimed sweep steps this long while sampling the "
+                         "gfx clock (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise kernel that reads and "
                          "writes this many MiB (calibrates HBM byte counters)")
@@ -535,12 +607,39 @@ def main(argv=None):
     flops_step = sum(c["fwd_f"] + c["bwd_f"] for c in cases)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
+    # The sustained clock under this load: untimed steps of the same sweep
+    # right after the timed region, with amdsmi sampling the gfx clock.
+    clock = None
+    if args.clock_seconds > 0:
+        sampler = gfx_clock_sampler()
+        if sampler is not None:
+            start_s, finish_s = sampler
+            start_s()
+            t_end = time.perf_counter() + args.clock_seconds
+            while time.perf_counter() < t_end:
+                for _ in range(5):
+                    step(False)
+                torch.cuda.synchronize()
+            samples = finish_s()
+            if samples:
+                mhz = statistics.median(samples)
+                clock = {"gfx_mhz_median": round(mhz, 1), "gfx_mhz_min": round(min(samples), 1),
+                         "gfx_mhz_max": round(max(samples), 1), "samples": len(samples),
+                         "source": f"amdsmi, {args.clock_seconds:g} s of untimed sweep steps "
+                                   "after the timed region",
+                         "mfma_peak_at_this_clock_tflops": round(
+                             torch.cuda.get_device_properties(0).multi_processor_count
+                             * mhz * 1e6 * 4096 / 1e12, 1)}
+
     per_config = {}
     for c in cases:
         w = c["w"]
-        fwd_ms = sum(e["f0"].elapsed_time(e["f1"]) for e in c["ev"]) / len(c["ev"])
-        bwd_ms = sum(e["f1"].elapsed_time(e["b1"]) for e in c["ev"]) / len(c["ev"])
-        dkdv_ms = sum(e["k0"].elapsed_time(e["k1"]) for e in c["ev"]) / len(c["ev"])
+        fwd_t = [e["f0"].elapsed_time(e["f1"]) for e in c["ev"]]
+        bwd_t = [e["f1"].elapsed_time(e["b1"]) for e in c["ev"]]
+        dkdv_t = [e["k0"].elapsed_time(e["k1"]) for e in c["ev"]]
+        fwd_ms = sum(fwd_t) / len(fwd_t)
+        bwd_ms = sum(bwd_t) / len(bwd_t)
+        dkdv_ms = sum(dkdv_t) / len(dkdv_t)
         per_config[w.name] = {
             "shape": w.describe(),
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
@@ -551,6 +650,16 @@ def main(argv=None):
             "bwd_tflops": round(c["bwd_f"] / bwd_ms / 1e9, 2),
             "fwd_pct_peak": round(100 * c["fwd_f"] / fwd_ms / 1e9 / PEAK_MFMA_TFLOPS, 2),
             "bwd_pct_peak": round(100 * c["bwd_f"] / bwd_ms / 1e9 / PEAK_MFMA_TFLOPS, 2),
+            # Per-launch statistics of the same event pairs (the means above
+            # include every timed step).
+            "fwd_ms_median": round(statistics.median(fwd_t), 4), "fwd_ms_min": round(min(fwd_t), 4),
+            "bwd_ms_median": round(statistics.median(bwd_t), 4), "bwd_ms_min": round(min(bwd_t), 4),
+            "bwd_dkdv_kernel_ms_median": round(statistics.median(dkdv_t), 4),
+            "bwd_dkdv_kernel_ms_min": round(min(dkdv_t), 4),
+            "fwd_pct_peak_at_median": round(
+                100 * c["fwd_f"] / statistics.median(fwd_t) / 1e9 / PEAK_MFMA_TFLOPS, 2),
+            "bwd_pct_peak_at_median": round(
+                100 * c["bwd_f"] / statistics.median(bwd_t) / 1e9 / PEAK_MFMA_TFLOPS, 2),
         }
 
     roofline = None
@@ -559,14 +668,23 @@ def main(argv=None):
     if dom is not None:
         dkdv_ms = per_config[DOMINANT]["bwd_dkdv_kernel_ms"]
         achieved = dom["bwd_f"] / dkdv_ms / 1e9
+        adds = dq_atomic_adds(dom["w"])
+        rate = adds / dkdv_ms / 1e6
+        # What limits the kernel, from this run's numbers: its dQ atomics
+        # against the memory-side atomic rate, else the matrix cores.
+        limiter = ("dq atomics (memory-side)" if rate >= 0.8 * DQ_ATOMIC_PROBE_G_PER_S
+                   else "matrix cores / latency")
         roofline = {"bound": "mfma", "kernel": "bwd_dkdv_kernel",
                     "workload": dom["w"].describe(),
                     "flops_per_launch": dom["bwd_f"],
                     "avg_launch_ms": dkdv_ms,
                     "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                    "traffic": traffic_record()}
-        adds = dq_atomic_adds(dom["w"])
+                    "traffic": traffic_record(),
+                    "limited_by": {"what": limiter,
+                                   "dq_atomic_g_per_s": round(rate, 1),
+                                   "atomic_probe_g_per_s": DQ_ATOMIC_PROBE_G_PER_S,
+                                   "frac_of_atomic_rate": round(rate / DQ_ATOMIC_PROBE_G_PER_S, 3)}}
         atomics = {"kernel": "bwd_dkdv_kernel", "workload": dom["w"].describe(),
                    "adds_per_launch": adds, "bytes_per_add": 4,
                    "avg_launch_ms": dkdv_ms,
@@ -630,6 +748,7 @@ def main(argv=None):
             f"{c['w'].name}: {c['w'].describe()}" for c in cases),
             "flops_per_step": flops_step},
         "pct_of_peak": round(100 * value / PEAK_MFMA_TFLOPS, 2),
+        "clock": clock,
         "roofline": roofline,
         "dq_atomics": atomics,
         "cpu_baseline": cpu,

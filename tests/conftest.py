@@ -28,3 +28,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    import oband
+    if oband.REPORT:
+        terminalreporter.write_sep("-", "forward output error by |O| band")
+        for line in oband.REPORT:
+            terminalreporter.write_line(line)

@@ -374,3 +374,34 @@ def test_noalloc_rejects_before_launch():
     assert call(B=1, H=16, Nq=16384, Nk=16384, D=64, causal=1) == _lib.FA_ERR_TOO_LARGE
     assert call(B=1, H=8, Nq=16384, Nk=16384, D=128) == _lib.FA_ERR_TOO_LARGE
     assert b"TOO_LARGE" in lib.fa_status_str(_lib.FA_ERR_TOO_LARGE)
+
+
+def _device_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_device_visible(), reason="needs a host without a visible GPU: the "
+                    "arguments are valid but the pointers are not device memory")
+def test_hip_error_without_device():
+    """With valid arguments and no device, every entry point that launches
+    returns FA_ERR_HIP (the launch, or the device lookup of the no-alloc
+    backward, fails), instead of crashing or reporting success."""
+    lib = _lib.load()
+    bf = _lib.FA_BF16
+    assert lib.fa_fwd(P, P, P, P, P, 1, 1, 128, 64, 0, 0.125, bf, None, None) == _lib.FA_ERR_HIP
+    assert lib.fa_fwd_qk(P, P, P, P, P, 1, 1, 64, 128, 128, 1, 0.1, bf, None,
+                         None) == _lib.FA_ERR_HIP
+    assert lib.fa_bwd(*([P] * 9), 1, 1, 128, 64, 0, 0.125, bf, None, P, 1 << 30,
+                      None) == _lib.FA_ERR_HIP
+    assert lib.fa_bwd_noalloc(*([P] * 9), 1, 1, 128, 128, 64, 0, 0.125, bf, None,
+                              None) == _lib.FA_ERR_HIP
+    assert lib.fa_merge(P, P, 2, P, P, 1, 1, 64, 64, bf, None) == _lib.FA_ERR_HIP
+    assert lib.fa_fwd_fp8(P, P, P, P, P, None, None, None, 1, 1, 128, 128, 64, 0, 0.125, bf,
+                          None, None) == _lib.FA_ERR_HIP
+    assert lib.fa_fwd_split(P, P, P, P, P, 1, 1, 1, 8192, 64, 1, 0.125, bf, None, 4, P,
+                            1 << 30, None) == _lib.FA_ERR_HIP
+    assert b"HIP" in lib.fa_status_str(_lib.FA_ERR_HIP)

@@ -5,9 +5,9 @@ split count from a fixed generator, runs the forward (fa.fwd, key-split
 when drawn) and the backward through the binding, and compares O, LSE,
 dQ, dK and dV with the fp64 oracle: LSE max-abs <= 1e-3 (rows that see no
 key exactly O = 0, LSE = -inf), each gradient max-abs <= 5e-2 *
-max|reference|, and O element by element within 1e-2 plus the rounding of
-the exact value to the output type, 2^-8 |O| for bf16 (2^-11 |O| for
-fp16).  The rounding term matters where a drawn scale makes rows peaked
+max|reference|, and O element by element within 1e-2 where |O| < 4, and
+where |O| >= 4 within 1e-2 plus the rounding of the exact value to the
+output type, 2^-8 |O| for bf16 (2^-11 |O| for fp16).  The rounding term matters where a drawn scale makes rows peaked
 enough for |O| to reach 4, where the bf16 spacing is 2^-5: there no bf16
 output can be within 1e-2 of every exact value (the first run of this
 sample failed the plain bar exactly at elements the kernel rounded to
@@ -24,6 +24,7 @@ import pytest
 import torch
 
 import io_aware_exact_02_amd as fa
+import oband
 from oracle import attention as oa
 from workloads import random_qkv
 
@@ -74,7 +75,14 @@ def test_random_shape(i, B, H, Nq, Nk, D, causal, dtype, scale, splits):
     if empty.any():
         assert np.all(o[np.transpose(empty, (0, 2, 1))] == 0.0), f"{what}: empty rows not 0"
     assert np.all(np.isfinite(o)), what
-    over = np.abs(o - O) - (O_TOL + RND[dtype] * np.abs(O))
+    err = np.abs(o - O)
+    small = np.abs(O) < 4.0
+    if small.any():
+        es = np.max(err[small])
+        assert es <= O_TOL, f"{what}: O max-abs {es:.3e} where |O| < 4"
+    if not small.all():
+        oband.record(f"random case {i}", o, O)
+    over = err - (O_TOL + RND[dtype] * np.abs(O))
     assert np.all(over <= 0), f"{what}: O over the bar by {np.max(over):.3e}"
     if (~empty).any():
         el = np.max(np.abs(lse[~empty] - LSE[~empty]))
