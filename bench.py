@@ -541,7 +541,7 @@ def main(argv=None):
 
     import torch
     import io_aware_exact_02_amd as fa
-    from workloads import WORKLOADS, make_inputs
+    from workloads import PROFILE_SHAPES, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -550,7 +550,7 @@ def main(argv=None):
     names = [n.strip() for n in args.workloads.split(",") if n.strip()]
     cases = []
     for name in names:
-        w = WORKLOADS[name]
+        w = WORKLOADS[name] if name in WORKLOADS else PROFILE_SHAPES[name]
         inp = make_inputs(w)
         c = {"w": w, "inp": inp}
         if w.layout == "packed":

@@ -212,10 +212,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  // Work item (kblk * nseg + seg) of head bh (xcd_item): heaviest key blocks
+  // first.
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
-  // blockIdx.x = (kblk * nseg + seg) * BH + bh: heaviest key blocks first.
-  const int item = static_cast<int>(blockIdx.x / BH);
+  const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_kblocks * (SEG ? p.nseg : 1));
+  if (!wg.valid) return;
+  const int bh = wg.bh;
+  const int item = wg.item;
   const int kblk = SEG ? item / p.nseg : item;
   const int seg = SEG ? item % p.nseg : 0;
   const int b = bh / p.H;
@@ -704,7 +707,7 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (stages & 2u) {
-    const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_kblocks * p.nseg;
+    const int64_t blocks = xcd_grid(p.B * p.H, p.num_kblocks * p.nseg);
     if (CAUSAL && p.nseg > 1) {  // only causal launches use query segments
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, CAUSAL>),
                          dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);

@@ -100,8 +100,17 @@ void fwd_kernel(FwdParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  // Query blocks of this workgroup, heaviest first.  Causal split launches
+  // pair block i with block n-1-i so that every workgroup does the same work.
+  // Work item rest = ks * slots + slot of head bh (xcd_item), with ks the key
+  // split: this workgroup sees keys [kv_lo, kv_hi) only.
+  constexpr bool PAIRED = CAUSAL && SPLIT;
+  const int slots = PAIRED ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
+  const XcdItem wg = xcd_item(blockIdx.x, BH, slots * p.num_splits);
+  if (!wg.valid) return;
+  const int bh = wg.bh;
+  const int rest = wg.item;
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;    // query rows
@@ -109,14 +118,6 @@ void fwd_kernel(FwdParams p) {
   const int off = p.off;
   const int g = SPLIT ? wave / Cfg::RW : 0;   // key group
   const int rw = SPLIT ? wave % Cfg::RW : wave;
-
-  // Query blocks of this workgroup, heaviest first.  Causal split launches
-  // pair block i with block n-1-i so that every workgroup does the same work.
-  // blockIdx.x = (ks * slots + slot) * BH + bh, with ks the key split: this
-  // workgroup sees keys [kv_lo, kv_hi) only.
-  constexpr bool PAIRED = CAUSAL && SPLIT;
-  const int slots = PAIRED ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
-  const int rest = static_cast<int>(blockIdx.x / BH);
   const int slot = rest % slots;
   const int ks = rest / slots;
   const int kv_lo = ks * p.split_len;
@@ -448,7 +449,7 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   p.num_qblocks = (p.N + BR - 1) / BR;
   // Causal split launches run blocks i and n-1-i in one workgroup.
   const int slots = CAUSAL && SPLIT ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * slots * p.num_splits;
+  const int64_t blocks = xcd_grid(p.B * p.H, slots * p.num_splits);
   hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPLIT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();

@@ -73,17 +73,18 @@ void fwd64_kernel(FwdParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  // Work item rest = ks * num_qblocks + slot of head bh (xcd_item); query
+  // blocks heaviest first; split ks covers keys [kv_lo, kv_hi).
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
+  const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_qblocks * p.num_splits);
+  if (!wg.valid) return;
+  const int bh = wg.bh;
+  const int rest = wg.item;
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;    // query rows
   const int Nk = p.Nk;  // keys; causal: query i sees keys j <= i + off
   const int off = p.off;
-
-  // blockIdx.x = (ks * num_qblocks + slot) * BH + bh; query blocks heaviest
-  // first; split ks covers keys [kv_lo, kv_hi).
-  const int rest = static_cast<int>(blockIdx.x / BH);
   const int slot = rest % p.num_qblocks;
   const int ks = rest / p.num_qblocks;
   const int kv_lo = ks * p.split_len;
@@ -434,7 +435,7 @@ template <typename T, int NW, bool CAUSAL>
 static hipError_t launch_fwd64_nw(const FwdParams& p_in, hipStream_t s) {
   FwdParams p = p_in;
   p.num_qblocks = (p.N + 32 * NW - 1) / (32 * NW);
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * p.num_qblocks * p.num_splits;
+  const int64_t blocks = xcd_grid(p.B * p.H, p.num_qblocks * p.num_splits);
   hipLaunchKernelGGL((fwd64_kernel<T, NW, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();

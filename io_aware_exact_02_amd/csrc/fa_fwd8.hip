@@ -125,8 +125,14 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
+  // Query blocks of this workgroup, heaviest first; causal split launches
+  // pair block i with block n-1-i.  Work item slot of head bh (xcd_item).
+  constexpr bool PAIRED = CAUSAL && SPLIT;
   const int BH = p.B * p.H;
-  const int bh = blockIdx.x % BH;
+  const XcdItem wg = xcd_item(blockIdx.x, BH, PAIRED ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
+  if (!wg.valid) return;
+  const int bh = wg.bh;
+  const int slot = wg.item;
   const int b = bh / p.H;
   const int h = bh % p.H;
   const int N = p.N;
@@ -134,10 +140,6 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
   const int off = Nk - N;  // causal: query i sees keys j <= i + off
   const int g = SPLIT ? wave / Cfg::RW : 0;  // key group
   const int rw = SPLIT ? wave % Cfg::RW : wave;
-  // Query blocks of this workgroup, heaviest first; causal split launches
-  // pair block i with block n-1-i.
-  constexpr bool PAIRED = CAUSAL && SPLIT;
-  const int slot = static_cast<int>(blockIdx.x / BH);
   const int blk_hi = p.num_qblocks - 1 - slot;
   const int nblk = PAIRED && slot != blk_hi ? 2 : 1;
 
@@ -423,7 +425,7 @@ static hipError_t launch_fwd8_nw(const Fwd8Params& p_in, hipStream_t s) {
   constexpr int BR = Fwd8Cfg<D, NW, SPLIT>::BR;
   p.num_qblocks = (p.N + BR - 1) / BR;
   const int slots = CAUSAL && SPLIT ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
-  const int64_t blocks = static_cast<int64_t>(p.B) * p.H * slots;
+  const int64_t blocks = xcd_grid(p.B * p.H, slots);
   hipLaunchKernelGGL((fwd8_kernel<T, D, NW, CAUSAL, SPLIT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();

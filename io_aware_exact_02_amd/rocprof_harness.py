@@ -48,7 +48,7 @@ BENCH = os.path.join(ROOT, "bench.py")
 PEAK_TFLOPS = 2516.6
 PEAK_FP8_TFLOPS = 5033.2
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_02_amd", "csrc", f)
-                  for f in ("fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp")]
+                  for f in ("fa_bwd.hip", "fa_device.hpp", "fa_kernels.hpp", "fa_xcd.hpp")]
 
 
 def source_hash() -> str:

@@ -170,6 +170,21 @@ def test_full_size_sampled(name, B, H, N, D):
         assert np.all(np.abs(o[0, rows, h] - r["O"]) <= r["bound"]), f"{name} h{h} O"
 
 
+@pytest.mark.parametrize("D,causal", [(64, True), (128, True), (128, False)])
+def test_twelve_heads(D, causal):
+    """B*H = 12, not a multiple of the 8 XCDs: the workgroup id -> (head,
+    block) mapping with ids past the last block.  Exact-weight inputs,
+    several blocks and a ragged tail."""
+    what = f"fp8 B=2 H=6 D={D} causal={causal}"
+    _say("case", what)
+    d = fp8_exact_weight_inputs(2, 1100, 1100, 6, D, 8700 + D + int(causal))
+    o, lse = _run(d, causal, d["scale"])
+    O, LSE = o8.attention_forward_fp8(*_args(d), causal=causal, scale=d["scale"])
+    _check_lse_and_empty(o, lse, O, LSE, what)
+    vmax = np.abs(o8._descaled(d["v"], d["descale_v"])).max()
+    assert np.all(np.abs(o - O) <= 2.0 ** -8 * np.abs(O) + 1e-4 * vmax), what
+
+
 @pytest.mark.parametrize("Nq,Nk", [(1024, 1024), (1100, 1100), (1100, 1500), (1500, 1100)])
 def test_split_paired_head_dim_128(Nq, Nk):
     """Causal head_dim-128 launches whose workgroups all fit on the device at

@@ -72,14 +72,16 @@ def assert_grad(name, got, ref, what=""):
 
 
 def assert_o_bar(o, O, rnd, what=""):
-    """The output bar of inputs whose exact output reaches |O| >= 4: there
-    no bf16 value need lie within 1e-2 of O, so the bar is 1e-2 plus the
-    rounding of O itself, 1e-2 + rnd |O|.  Below |O| = 4 it is the plain
-    1e-2."""
+    """The output bar of inputs whose exact output reaches |O| >= 2.  There
+    the rounding of O itself to the output type (half a spacing, 2^-9 |O|
+    for bf16) and that of the softmax weights before the P V product (at
+    most 2^-9 max|v|) can together pass 1e-2, and at |O| >= 4 no bf16 value
+    need lie within 1e-2 of O: the bar is 1e-2 + rnd |O| (rnd = 2^-8 for
+    bf16, 2^-11 for fp16).  Below |O| = 2 it is the plain 1e-2."""
     err = np.abs(o - O)
-    big = np.abs(O) >= 4.0
+    big = np.abs(O) >= 2.0
     small_err = np.max(err[~big]) if (~big).any() else 0.0
-    assert small_err <= O_TOL, f"{what} O max-abs {small_err:.3e} where |O| < 4"
+    assert small_err <= O_TOL, f"{what} O max-abs {small_err:.3e} where |O| < 2"
     over = err - (O_TOL + rnd * np.abs(O))
     assert np.all(over <= 0), f"{what} O over the bar by {np.max(over):.3e}"
 
@@ -134,10 +136,10 @@ def test_peaked_softmax(D, causal, dtype):
     Output bar: such rows are close to a single V row, so |O| reaches
     max|v| (about 4.2 to 4.8 here), where rounding the exact result to bf16
     alone costs up to 2^-8 |O| > 1e-2 (measured: the largest errors are
-    exactly the exact result's own bf16 rounding).  Where |O| >= 4 the bar is
-    the 1e-2 budget plus that rounding, |o - O| <= 1e-2 + 2^-8 |O| (2^-11 |O|
-    for fp16); below 4 it stays 1e-2.  LSE and gradients keep the usual
-    bars."""
+    exactly the exact result's own bf16 rounding).  Where |O| >= 2 the bar
+    is the 1e-2 budget plus the roundings, |o - O| <= 1e-2 + 2^-8 |O|
+    (2^-11 |O| for fp16); below 2 it stays 1e-2.  LSE and gradients keep
+    the usual bars."""
     what = f"peaked D={D} causal={causal} {dtype}"
     _say("case", what)
     inp = random_qkv(2, 333, 2, D, dtype, seed=7150 + D)
@@ -172,6 +174,27 @@ def test_strided_bhnd_input(D):
     for name in ("q", "k", "v", "do"):
         inp[name] = inp[name].transpose(1, 2).contiguous().transpose(1, 2)
     check_full(inp, True, what=f"strided D={D}")
+
+
+@pytest.mark.parametrize("B,H,D,causal", [(1, 3, 64, True), (1, 12, 128, True),
+                                           (3, 5, 64, False), (1, 12, 64, True)])
+def test_head_counts_off_the_xcd_grid(B, H, D, causal):
+    """B*H of 3, 12 and 15 heads: workgroup ids map to (head, block) so that
+    each head stays on few XCDs, with ids past the last block exiting at
+    once.  Forward, key-split forward (3 splits) and backward against the
+    oracle over several blocks and a ragged tail, so every (head, block)
+    pair of each grid is checked."""
+    what = f"B={B} H={H} D={D} causal={causal}"
+    _say("case xcd map", what)
+    inp = random_qkv(B, 700, H, D, "bf16", seed=7900 + 16 * B + H + D)
+    check_full(inp, causal, what=what)
+    dev = torch.device("cuda")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal, num_splits=3)
+    torch.cuda.synchronize()
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=causal)
+    got = {"O": o.to("cpu", torch.float64).numpy(), "LSE": lse.to("cpu", torch.float64).numpy()}
+    assert_forward(got, O, LSE, what + " split 3")
 
 
 # ------------------------------------------------------------ the five configs

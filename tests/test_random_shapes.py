@@ -5,13 +5,16 @@ split count from a fixed generator, runs the forward (fa.fwd, key-split
 when drawn) and the backward through the binding, and compares O, LSE,
 dQ, dK and dV with the fp64 oracle: LSE max-abs <= 1e-3 (rows that see no
 key exactly O = 0, LSE = -inf), each gradient max-abs <= 5e-2 *
-max|reference|, and O element by element within 1e-2 where |O| < 4, and
-where |O| >= 4 within 1e-2 plus the rounding of the exact value to the
-output type, 2^-8 |O| for bf16 (2^-11 |O| for fp16).  The rounding term matters where a drawn scale makes rows peaked
-enough for |O| to reach 4, where the bf16 spacing is 2^-5: there no bf16
-output can be within 1e-2 of every exact value (the first run of this
-sample failed the plain bar exactly at elements the kernel rounded to
-bf16(O) itself).  The sample crosses options
+max|reference|, and O element by element within 1e-2 where |O| < 2 and,
+where |O| >= 2, within 1e-2 plus 2^-8 |O| for bf16 (2^-11 |O| for fp16):
+the rounding of the exact value to the output type (half a spacing, 2^-9
+|O|) plus that of the softmax weights before the P V product (at most
+2^-9 max|v|).  Below |O| = 2 the output's rounding costs at most 3.9e-3 and
+the plain bar keeps its margin; at |O| >= 4 no bf16 value need lie within
+1e-2 of the exact one (the first run of this sample failed the plain bar
+exactly at elements the kernel rounded to bf16(O) itself), and in [2, 4)
+the two roundings together reach 1.0e-2 (seen once in this sample).  Cases
+with |O| >= 2 report their error per |O| band.  The sample crosses options
 that the grid tests take one at a time (unequal lengths with a negative
 scale and a key split, ragged tails on both sides, one-row problems).
 """
@@ -76,12 +79,12 @@ def test_random_shape(i, B, H, Nq, Nk, D, causal, dtype, scale, splits):
         assert np.all(o[np.transpose(empty, (0, 2, 1))] == 0.0), f"{what}: empty rows not 0"
     assert np.all(np.isfinite(o)), what
     err = np.abs(o - O)
-    small = np.abs(O) < 4.0
-    if small.any():
-        es = np.max(err[small])
-        assert es <= O_TOL, f"{what}: O max-abs {es:.3e} where |O| < 4"
+    small = np.abs(O) < 2.0
     if not small.all():
         oband.record(f"random case {i}", o, O)
+    if small.any():
+        es = np.max(err[small])
+        assert es <= O_TOL, f"{what}: O max-abs {es:.3e} where |O| < 2"
     over = err - (O_TOL + RND[dtype] * np.abs(O))
     assert np.all(over <= 0), f"{what}: O over the bar by {np.max(over):.3e}"
     if (~empty).any():

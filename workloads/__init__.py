@@ -75,6 +75,15 @@ PAGES_SWEEP = {
 }
 
 
+# Shapes for profiling the workgroup -> XCD mapping: 12 heads, a count the
+# eight XCDs do not divide (each XCD's L2 serves two of them rather than
+# three), causal, at head_dim 64 and 128.
+PROFILE_SHAPES = {
+    "h12": Workload("h12", 1, 12, 8192, 64, "bf16", True, "bnhd", 1212),
+    "h12d128": Workload("h12d128", 1, 12, 8192, 128, "bf16", True, "bnhd", 1213),
+}
+
+
 def _randn(shape, gen: torch.Generator, dtype: torch.dtype) -> torch.Tensor:
     return torch.randn(shape, dtype=torch.float32, generator=gen).to(dtype)
 
