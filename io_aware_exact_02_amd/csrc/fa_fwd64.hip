@@ -54,6 +54,7 @@ void fwd64_kernel(FwdParams p) {
   constexpr int DB = D / 32;                 // 32-wide d blocks of O
   constexpr int TILE = BC * D;               // halves per K (or V) tile
   static_assert(NCH * THREADS == BC * CPR, "tile load must divide evenly");
+  static_assert(KC + 2 * DB == 8, "a pipeline step holds eight MFMAs");
 
   // Three K and three V buffers, each its own LDS object so that the
   // asynchronous loads into one are known not to alias reads of another.
@@ -240,13 +241,9 @@ void fwd64_kernel(FwdParams p) {
                     pack2<T>(s[6], s[7])};
     pp[1] = (u32x4){pack2<T>(s[8], s[9]), pack2<T>(s[10], s[11]), pack2<T>(s[12], s[13]),
                     pack2<T>(s[14], s[15])};
-    lbt = sum2_acc<T>(pp[0][0], 0.0f);
-    lbt = sum2_acc<T>(pp[1][0], lbt);
+    lbt = 0.0f;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      lbt = sum2_acc<T>(pp[0][w], lbt);
-      lbt = sum2_acc<T>(pp[1][w], lbt);
-    }
+    for (int w = 0; w < 8; ++w) lbt = sum2_acc<T>(pp[w / 4][w % 4], lbt);
   };
   // The rare step that moves m: S of half k is recomputed from its K rows
   // (kt; still in LDS), m becomes the running row maximum, the accumulators
@@ -294,9 +291,56 @@ void fwd64_kernel(FwdParams p) {
     u32x4(&pcur)[2] = (I % 2 == 0) ? pa : pb;
     u32x4(&pprev)[2] = (I % 2 == 0) ? pb : pa;
     float lt, lbt;
-    nxt = s_half(kbuf(IntC<KB>{}) + 32 * KH * D);
-    pv_half(vbuf(IntC<VB>{}) + 32 * VH * D, pprev);
-    weights(cur, pcur, lt, lbt);
+    if constexpr (NW == 8) {
+      // Left to itself the compiler issues the step's eight MFMAs together
+      // and the softmax after them, each MFMA right behind the LDS read of
+      // its operand.  Here the step runs as eight chunks, each holding the
+      // LDS read of the next chunk's operand, one MFMA (the four of
+      // S(H_{k+1}), then the four of the PV product of H_{k-1}) and the
+      // weights of two scores of H_k, fenced so that the order holds: each
+      // MFMA runs while its chunk's vector work issues.  The sums are those
+      // of weights(), in the same order.  (About 5% faster than the grouped
+      // order at B=1 H=16 N=16384 causal; 4-wave launches, with more
+      // registers per wave and fewer waves per SIMD, run slower this way.)
+      const uint16_t* kt = kbuf(IntC<KB>{}) + 32 * KH * D;
+      const uint16_t* vt = vbuf(IntC<VB>{}) + 32 * VH * D;
+      const float negm = -fmaxf(m, -3.0e38f);
+      f32x16 acc = (f32x16){};
+      float s0 = 0.0f, s1 = 0.0f;
+      lbt = 0.0f;
+      auto operand = [&](int j) -> u32x4 {
+        if (j < KC) return lds_ld16(kt, k_off[j]);
+        const int cc = (j - KC) / DB, db = (j - KC) % DB;
+        return lds_tr16(vt + 16 * cc * D, v_off[0][db], v_off[1][db]);
+      };
+      u32x4 opnd = operand(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4 next = opnd;
+        if (j + 1 < 8) next = operand(j + 1);
+        if (j < KC) {
+          acc = mfma32x32x16<T>(opnd, qreg[j], acc);
+        } else {
+          const int cc = (j - KC) / DB, db = (j - KC) % DB;
+          oacc[db] = mfma32x32x16<T>(opnd, pprev[cc], oacc[db]);
+        }
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(cur[2 * j], c_scale, negm));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(cur[2 * j + 1], c_scale, negm));
+        s0 += e0;
+        s1 += e1;
+        const uint32_t pk = pack2<T>(e0, e1);
+        pcur[j / 4][j % 4] = pk;
+        lbt = sum2_acc<T>(pk, lbt);
+        opnd = next;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      nxt = acc;
+      lt = s0 + s1;
+    } else {
+      nxt = s_half(kbuf(IntC<KB>{}) + 32 * KH * D);
+      pv_half(vbuf(IntC<VB>{}) + 32 * VH * D, pprev);
+      weights(cur, pcur, lt, lbt);
+    }
     if (__any(!(lt <= 256.0f))) {
       // Keeps this rarely taken block a real branch.
       asm volatile("" ::: "memory");
