@@ -11,6 +11,8 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# The same library built with LDS poisoning (FA_POISON_LDS=1), for tests.
+POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_poison.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 FA_F16, FA_BF16 = 0, 1
@@ -47,13 +49,18 @@ _lib = None
 def load() -> ctypes.CDLL:
     """Load libfa.so once; raise ImportError if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+    if _lib is None:
+        _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at ``path`` and declare its signatures."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} not found: build the HIP library first "
+            f"{path} not found: build the HIP library first "
             "(python -m io_aware_exact_02_amd.build)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                            ctypes.POINTER(FwdStrides), vp]
@@ -96,7 +103,6 @@ def load() -> ctypes.CDLL:
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

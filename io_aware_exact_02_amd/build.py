@@ -3,7 +3,8 @@
     python -m io_aware_exact_02_amd.build [--verbose]
 
 Each source is compiled by hipcc into an object under ``_build/`` and the
-objects are linked into ``io_aware_exact_02_amd/libfa.so`` next to this file.
+objects are linked into ``io_aware_exact_02_amd/libfa.so`` next to this file;
+a second build with LDS poisoning goes to ``libfa_poison.so`` (tests only).
 Always recompiles (the build check must exercise the compiler every time).
 """
 
@@ -21,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+POISON_LIB = os.path.join(PKG, "libfa_poison.so")
 
 SOURCES = ["fa_fwd.hip", "fa_fwd64.hip", "fa_fwd8.hip", "fa_bwd.hip", "fa_merge.hip", "fa_api.cpp"]
 ARCH = "gfx950"
@@ -54,29 +56,38 @@ def _run(cmd, verbose):
     return res
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link libfa.so; returns the library path."""
+def build(verbose: bool = False, extra_flags=(), poison: bool = False) -> str:
+    """Compile every source and link libfa.so; returns the library path.
+
+    ``poison=True`` builds libfa_poison.so instead: the same kernels with
+    every LDS array filled with NaN bits when a workgroup starts
+    (FA_POISON_LDS), for the tests that look for reads of unwritten LDS."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    out_lib = POISON_LIB if poison else LIB
+    obj_dir = os.path.join(BUILD, "poison") if poison else BUILD
+    if poison:
+        extra_flags = (*extra_flags, "-DFA_POISON_LDS=1")
+    os.makedirs(obj_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.rsplit(".", 1)[0] + ".o")
+        obj = os.path.join(obj_dir, src.rsplit(".", 1)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmds.append([hipcc, *COMMON, *extra_flags, *lang, "-c",
                      os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = out_lib + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     # Loading resolves every symbol: a kernel whose host launch stub was not
     # emitted fails here, not at the first call.
     import ctypes
     ctypes.CDLL(tmp)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, poison=True))

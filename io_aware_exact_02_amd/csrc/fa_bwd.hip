@@ -129,6 +129,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
     kmax = fmaxf(kmax, __shfl_xor(kmax, off, 64));
   }
   __shared__ float red[4][3];
+  poison_lds(red);
   if ((tid & 63) == 0) {
     red[tid >> 6][0] = donorm;
     red[tid >> 6][1] = kmax;
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int BH = p.B * p.H;
   const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_kblocks * (SEG ? p.nseg : 1));
   if (!wg.valid) return;
+  poison_lds(Ks, Qs, dOs, dSt, lse_s, ndv_s);
   const int bh = wg.bh;
   const int item = wg.item;
   const int kblk = SEG ? item / p.nseg : item;
@@ -263,6 +265,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   float dq_scale;
   {
     __shared__ float red[NW][3];
+    poison_lds(red);
     const float* part = p.bound_part + static_cast<int64_t>(bh) * 3 * p.npart;
     float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f;
     for (int c = tid; c < p.npart; c += THREADS) {

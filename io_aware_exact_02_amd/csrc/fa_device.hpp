@@ -313,6 +313,31 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
 
+// LDS poisoning for debug builds (compiled with -DFA_POISON_LDS=1, as
+// libfa_poison.so): every LDS array of a kernel is filled with all-ones bits
+// -- a NaN as bf16, f16, fp32 and E4M3 -- when the workgroup starts, so a
+// read of LDS the kernel has not written reaches the outputs as NaN instead
+// of as whatever an earlier workgroup left there.  Every thread of the
+// workgroup must reach the call (it ends in a barrier).  A no-op otherwise.
+#ifndef FA_POISON_LDS
+#define FA_POISON_LDS 0
+#endif
+template <typename A>
+__device__ __forceinline__ void poison_one(A& a) {
+  static_assert(sizeof(A) % 4 == 0, "LDS arrays are whole words");
+  uint32_t* w = reinterpret_cast<uint32_t*>(&a);
+  for (int i = static_cast<int>(threadIdx.x); i < static_cast<int>(sizeof(A) / 4);
+       i += static_cast<int>(blockDim.x))
+    w[i] = 0xFFFFFFFFu;
+}
+template <typename... A>
+__device__ __forceinline__ void poison_lds(A&... arrays) {
+  if constexpr (FA_POISON_LDS != 0) {
+    (poison_one(arrays), ...);
+    __syncthreads();
+  }
+}
+
 template <int V>
 struct IntC {
   static constexpr int value = V;

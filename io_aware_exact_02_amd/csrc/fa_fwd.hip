@@ -109,6 +109,7 @@ void fwd_kernel(FwdParams p) {
   const int BH = p.B * p.H;
   const XcdItem wg = xcd_item(blockIdx.x, BH, slots * p.num_splits);
   if (!wg.valid) return;
+  poison_lds(Ks0, Ks1, Vs0, Vs1);
   const int bh = wg.bh;
   const int rest = wg.item;
   const int b = bh / p.H;

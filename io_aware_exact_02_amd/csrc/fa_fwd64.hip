@@ -79,6 +79,7 @@ void fwd64_kernel(FwdParams p) {
   const int BH = p.B * p.H;
   const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_qblocks * p.num_splits);
   if (!wg.valid) return;
+  poison_lds(Ks0, Ks1, Ks2, Vs0, Vs1, Vs2);
   const int bh = wg.bh;
   const int rest = wg.item;
   const int b = bh / p.H;

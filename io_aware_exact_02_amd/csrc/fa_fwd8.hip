@@ -131,6 +131,7 @@ __attribute__((amdgpu_waves_per_eu(Fwd8Occupancy<D>::value))) void fwd8_kernel(F
   const int BH = p.B * p.H;
   const XcdItem wg = xcd_item(blockIdx.x, BH, PAIRED ? (p.num_qblocks + 1) / 2 : p.num_qblocks);
   if (!wg.valid) return;
+  poison_lds(Ks0, Ks1, Vs0, Vs1, xs);
   const int bh = wg.bh;
   const int slot = wg.item;
   const int b = bh / p.H;

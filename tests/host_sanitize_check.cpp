@@ -1,0 +1,122 @@
+// Every C ABI entry point called from C++ through include/fa.h, for a build
+// of the host side under AddressSanitizer and UndefinedBehaviorSanitizer
+// (tests/test_host_sanitized.py).  Runs on the CPU: invalid arguments must
+// come back as their status codes without launching anything; with no GPU
+// visible, well-formed calls must return FA_ERR_HIP.  Prints "ok <checks>"
+// or the first mismatch (exit status 1); a sanitizer report aborts the run.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa.h"
+
+static int checks = 0;
+static int failed = 0;
+
+static void expect(int got, int want, const char* what) {
+  ++checks;
+  if (got != want && !failed) {
+    std::printf("FAIL %s: status %d (%s), expected %d\n", what, got, fa_status_str(got), want);
+    failed = 1;
+  }
+}
+
+int main() {
+  // Stand-in device addresses: aligned, never dereferenced on the host, and
+  // only passed where the call must stop before any launch.
+  void* const P = reinterpret_cast<void*>(static_cast<uintptr_t>(1) << 20);
+  float* const F = static_cast<float*>(P);
+  const int B = 2, H = 3, N = 100, D = 64;
+
+  // Status names and sizes.
+  for (int s = -1; s <= 5; ++s) {
+    ++checks;
+    if (fa_status_str(s) == nullptr || std::strlen(fa_status_str(s)) == 0) failed = 1;
+  }
+  ++checks;
+  if (std::strncmp(fa_version(), "fa-gfx950", 9) != 0) failed = 1;
+  ++checks;
+  if (fa_bwd_workspace_bytes(B, H, N, D) == 0 || fa_bwd_qk_workspace_bytes(B, H, N, 77, D) == 0 ||
+      fa_fwd_split_workspace_bytes(B, H, N, D, 3) == 0 || fa_bwd_noalloc_max_bytes() == 0)
+    failed = 1;
+  ++checks;
+  if (fa_bwd_workspace_bytes(-1, H, N, D) != 0 || fa_bwd_qk_workspace_bytes(B, H, N, N, 96) != 0)
+    failed = 1;
+  ++checks;
+  if (fa_fwd_split_count(B, H, N, N, D, 1) < 1) failed = 1;
+
+  // Invalid arguments: caught before any HIP call.
+  expect(fa_fwd(nullptr, P, P, P, F, B, H, N, D, 0, 0.125f, FA_BF16, nullptr, nullptr),
+         FA_ERR_INVALID_ARG, "fa_fwd null q");
+  expect(fa_fwd(P, P, P, P, F, B, H, -1, D, 0, 0.125f, FA_BF16, nullptr, nullptr),
+         FA_ERR_INVALID_ARG, "fa_fwd negative N");
+  expect(fa_fwd(P, P, P, P, F, B, H, N, 96, 0, 0.125f, FA_BF16, nullptr, nullptr),
+         FA_ERR_UNSUPPORTED, "fa_fwd head_dim 96");
+  expect(fa_fwd(P, P, P, P, F, B, H, N, D, 0, 0.125f, 7, nullptr, nullptr),
+         FA_ERR_INVALID_ARG, "fa_fwd dtype 7");
+  fa_fwd_strides bad{};
+  bad.q = {N * H * D, H * D, 3};  // head stride not a multiple of 8 elements
+  bad.k = bad.v = bad.o = {N * H * D, H * D, D};
+  expect(fa_fwd(P, P, P, P, F, B, H, N, D, 0, 0.125f, FA_BF16, &bad, nullptr),
+         FA_ERR_UNSUPPORTED, "fa_fwd misaligned stride");
+  expect(fa_fwd_qk(P, P, P, P, F, B, H, N, 0, D, 1, 0.125f, FA_F16, nullptr, nullptr),
+         FA_ERR_INVALID_ARG, "fa_fwd_qk Nk = 0");
+  // (1000 keys in 3 splits: a workspace is needed.)
+  expect(fa_fwd_split(P, P, P, P, F, B, H, N, 1000, D, 0, 0.125f, FA_BF16, nullptr, 3, P, 16,
+                      nullptr),
+         FA_ERR_INVALID_ARG, "fa_fwd_split small workspace");
+  expect(fa_fwd_fp8(P, P, P, P, F, F, F, F, B, H, N, N, 80, 0, 0.125f, FA_BF16, nullptr, nullptr),
+         FA_ERR_UNSUPPORTED, "fa_fwd_fp8 head_dim 80");
+  const size_t ws = fa_bwd_workspace_bytes(B, H, N, D);
+  expect(fa_bwd(P, P, P, P, P, F, P, P, P, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, P, ws - 1,
+                nullptr),
+         FA_ERR_INVALID_ARG, "fa_bwd small workspace");
+  expect(fa_bwd(P, P, P, P, P, nullptr, P, P, P, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, P, ws,
+                nullptr),
+         FA_ERR_INVALID_ARG, "fa_bwd null lse");
+  expect(fa_bwd_stages(P, P, P, P, P, F, P, P, P, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, P, ws,
+                       8u, nullptr),
+         FA_ERR_INVALID_ARG, "fa_bwd_stages stage 8");
+  expect(fa_bwd_qk(P, P, P, P, P, F, P, P, P, B, H, N, N, 128, 1, 0.125f, FA_F16, nullptr,
+                   nullptr, 0, FA_STAGE_ALL, nullptr),
+         FA_ERR_INVALID_ARG, "fa_bwd_qk null workspace");
+  expect(fa_bwd_noalloc(P, P, P, P, P, F, P, P, P, 64, 64, 16384, 16384, 128, 1, 0.125f, FA_BF16,
+                        nullptr, nullptr),
+         FA_ERR_TOO_LARGE, "fa_bwd_noalloc beyond its scratch");
+  expect(fa_merge(P, F, 0, P, F, B, H, N, D, FA_BF16, nullptr), FA_ERR_INVALID_ARG,
+         "fa_merge P = 0");
+
+  // Well-formed calls with no device: FA_ERR_HIP (skipped when a device is
+  // visible, since the stand-in addresses would then reach a kernel).
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
+    expect(fa_fwd(P, P, P, P, F, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, nullptr), FA_ERR_HIP,
+           "fa_fwd no device");
+    expect(fa_fwd_qk(P, P, P, P, F, B, H, N, 77, D, 0, 0.125f, FA_F16, nullptr, nullptr),
+           FA_ERR_HIP, "fa_fwd_qk no device");
+    const size_t sws = fa_fwd_split_workspace_bytes(B, H, N, D, 2);
+    expect(fa_fwd_split(P, P, P, P, F, B, H, N, N, D, 0, 0.125f, FA_BF16, nullptr, 2, P, sws,
+                        nullptr),
+           FA_ERR_HIP, "fa_fwd_split no device");
+    expect(fa_fwd_fp8(P, P, P, P, F, F, F, F, B, H, N, N, 128, 1, 0.125f, FA_BF16, nullptr,
+                      nullptr),
+           FA_ERR_HIP, "fa_fwd_fp8 no device");
+    expect(fa_bwd(P, P, P, P, P, F, P, P, P, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, P, ws,
+                  nullptr),
+           FA_ERR_HIP, "fa_bwd no device");
+    expect(fa_bwd_noalloc(P, P, P, P, P, F, P, P, P, B, H, N, N, D, 0, 0.125f, FA_F16, nullptr,
+                          nullptr),
+           FA_ERR_HIP, "fa_bwd_noalloc no device");
+    expect(fa_merge(P, F, 2, P, F, B, H, N, D, FA_BF16, nullptr), FA_ERR_HIP, "fa_merge no device");
+  } else {
+    std::printf("device visible: well-formed calls not made\n");
+  }
+  if (failed) {
+    std::printf("FAIL after %d checks\n", checks);
+    return 1;
+  }
+  std::printf("ok %d\n", checks);
+  return 0;
+}
