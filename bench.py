@@ -54,6 +54,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import threading
 import time
@@ -276,6 +277,8 @@ def fp8_forward(torch, fa, per_config):
     stream = torch.cuda.current_stream(dev)
     rows = {}
     for name, cfg in per_config.items():
+        if name not in WORKLOADS:  # profiling shapes: 16-bit only
+            continue
         w = WORKLOADS[name]
         d = fp8_random_inputs(w.B, w.N, w.N, w.H, w.D, 9100 + w.N)
         q, k, v = (d[n].to(dev) for n in ("q", "k", "v"))
@@ -444,8 +447,29 @@ def mha_layer(torch, fa):
 
 
 # Memory-side rate of 32-bit integer atomics measured with a throughput probe
-# on MI355X (any address pattern): the ceiling of the dQ accumulation.
+# on MI355X: the ceiling of the dQ accumulation.  Used only when the probe
+# program (built next to the library) cannot run; otherwise the rate is
+# measured in the same run.
 DQ_ATOMIC_PROBE_G_PER_S = 412.0
+PROBE = os.path.join(ROOT, "io_aware_exact_02_amd", "atomic_probe")
+
+
+def atomic_probe():
+    """Run the atomic throughput probe (a child process on the same GPU,
+    after the timed region): int32, paired-int64 and fp32 atomic adds in the
+    dQ accumulation pattern of c5.  Returns its JSON, or None."""
+    if not os.path.exists(PROBE):
+        return None
+    try:
+        res = subprocess.run([PROBE], capture_output=True, text=True, timeout=120)
+    except (OSError, subprocess.TimeoutExpired) as e:
+        return {"error": str(e)}
+    if res.returncode != 0:
+        return {"error": (res.stdout + res.stderr)[-300:]}
+    try:
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    except (ValueError, IndexError):
+        return {"error": res.stdout[-300:]}
 
 
 def gfx_clock_sampler():
@@ -525,6 +549,8 @@ def main(argv=None):
                     help="skip the key-split forward measurement")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the one-GPU share of c5 under 8-way head sharding")
+    ap.add_argument("--no-atomic-probe", dest="atomic_probe", action="store_false",
+                    help="do not run the atomic throughput probe after the timed region")
     ap.add_argument("--clock-seconds", type=float, default=1.0,
                     help="after timing, run untimed sweep steps this long while sampling the "
                          "gfx clock (0 = skip)")
@@ -631,6 +657,10 @@ def main(argv=None):
                              torch.cuda.get_device_properties(0).multi_processor_count
                              * mhz * 1e6 * 4096 / 1e12, 1)}
 
+    probe = atomic_probe() if args.atomic_probe else None
+    probe_rate = (probe or {}).get("i32_g_per_s")
+    atomic_ceiling = probe_rate if probe_rate else DQ_ATOMIC_PROBE_G_PER_S
+
     per_config = {}
     for c in cases:
         w = c["w"]
@@ -672,7 +702,7 @@ def main(argv=None):
         rate = adds / dkdv_ms / 1e6
         # What limits the kernel, from this run's numbers: its dQ atomics
         # against the memory-side atomic rate, else the matrix cores.
-        limiter = ("dq atomics (memory-side)" if rate >= 0.8 * DQ_ATOMIC_PROBE_G_PER_S
+        limiter = ("dq atomics (memory-side)" if rate >= 0.8 * atomic_ceiling
                    else "matrix cores / latency")
         roofline = {"bound": "mfma", "kernel": "bwd_dkdv_kernel",
                     "workload": dom["w"].describe(),
@@ -683,8 +713,10 @@ def main(argv=None):
                     "traffic": traffic_record(),
                     "limited_by": {"what": limiter,
                                    "dq_atomic_g_per_s": round(rate, 1),
-                                   "atomic_probe_g_per_s": DQ_ATOMIC_PROBE_G_PER_S,
-                                   "frac_of_atomic_rate": round(rate / DQ_ATOMIC_PROBE_G_PER_S, 3)}}
+                                   "atomic_probe_g_per_s": round(atomic_ceiling, 1),
+                                   "atomic_probe": probe if probe else
+                                   {"fixed_g_per_s": DQ_ATOMIC_PROBE_G_PER_S},
+                                   "frac_of_atomic_rate": round(rate / atomic_ceiling, 3)}}
         atomics = {"kernel": "bwd_dkdv_kernel", "workload": dom["w"].describe(),
                    "adds_per_launch": adds, "bytes_per_add": 4,
                    "avg_launch_ms": dkdv_ms,

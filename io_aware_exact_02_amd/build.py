@@ -4,7 +4,8 @@
 
 Each source is compiled by hipcc into an object under ``_build/`` and the
 objects are linked into ``io_aware_exact_02_amd/libfa.so`` next to this file;
-a second build with LDS poisoning goes to ``libfa_poison.so`` (tests only).
+a second build with LDS poisoning goes to ``libfa_poison.so`` (tests only),
+and the atomic throughput probe that bench.py runs to ``atomic_probe``.
 Always recompiles (the build check must exercise the compiler every time).
 """
 
@@ -23,6 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 POISON_LIB = os.path.join(PKG, "libfa_poison.so")
+PROBE = os.path.join(PKG, "atomic_probe")
 
 SOURCES = ["fa_fwd.hip", "fa_fwd64.hip", "fa_fwd8.hip", "fa_bwd.hip", "fa_merge.hip", "fa_api.cpp"]
 ARCH = "gfx950"
@@ -85,6 +87,10 @@ def build(verbose: bool = False, extra_flags=(), poison: bool = False) -> str:
     import ctypes
     ctypes.CDLL(tmp)
     os.replace(tmp, out_lib)
+    if not poison:
+        # The memory-side atomic throughput probe that bench.py runs.
+        _run([hipcc, *[f for f in COMMON if f != "-fPIC"], "-x", "hip",
+              os.path.join(CSRC, "atomic_probe.cpp"), "-o", PROBE], verbose)
     return out_lib
 
 

@@ -85,6 +85,9 @@ def run(cmd, timeout, log):
 def bench_cmd(workloads, steps, warmup, calib_mib):
     return [sys.executable, BENCH, "--steps", str(steps), "--warmup", str(warmup), "--cpu-seconds", "0",
             "--no-memory", "--no-pages-sweep", "--no-mha", "--no-shard", "--no-split",
+            # No kernels after the timed region: the summary's "timed" column
+            # takes each kernel's last dispatches.
+            "--clock-seconds", "0", "--no-atomic-probe",
             "--workloads", workloads,
             "--copy-calibration-mib", str(calib_mib)]
 
