@@ -77,7 +77,7 @@ void fwd64_kernel(FwdParams p) {
   // Work item rest = ks * num_qblocks + slot of head bh (xcd_item); query
   // blocks heaviest first; split ks covers keys [kv_lo, kv_hi).
   const int BH = p.B * p.H;
-  const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_qblocks * p.num_splits);
+  const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_qblocks * p.num_splits, p.snake != 0);
   if (!wg.valid) return;
   poison_lds(Ks0, Ks1, Ks2, Vs0, Vs1, Vs2);
   const int bh = wg.bh;
@@ -477,10 +477,15 @@ void fwd64_kernel(FwdParams p) {
 }
 
 template <typename T, int NW, bool CAUSAL>
-static hipError_t launch_fwd64_nw(const FwdParams& p_in, hipStream_t s) {
+static hipError_t launch_fwd64_nw(const FwdParams& p_in, bool masked, hipStream_t s) {
   FwdParams p = p_in;
   p.num_qblocks = (p.N + 32 * NW - 1) / (32 * NW);
   const int64_t blocks = xcd_grid(p.B * p.H, p.num_qblocks * p.num_splits);
+  // Resident workgroups per compute unit: two 8-wave ones (4 waves per
+  // SIMD), three 4-wave ones (LDS: 48 KB each).  A causal grid that fits
+  // runs at once, so its blocks go out in snake order (xcd_item).
+  const int64_t slots = 256 * (NW == 8 ? 2 : 3);
+  p.snake = masked && p.num_splits == 1 && blocks <= slots ? 1 : 0;
   hipLaunchKernelGGL((fwd64_kernel<T, NW, CAUSAL>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();
@@ -495,8 +500,8 @@ hipError_t launch_fwd64_t(const FwdParams& p_in, bool causal, hipStream_t s) {
   FwdParams p = p_in;
   if (!causal) p.off = p.Nk;
   const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
-  if (wg8 >= 512) return launch_fwd64_nw<T, 8, true>(p, s);
-  return launch_fwd64_nw<T, 4, true>(p, s);
+  if (wg8 >= 512) return launch_fwd64_nw<T, 8, true>(p, causal, s);
+  return launch_fwd64_nw<T, 4, true>(p, causal, s);
 }
 
 hipError_t launch_fwd64(const FwdParams& p, int dtype, bool causal, hipStream_t s) {

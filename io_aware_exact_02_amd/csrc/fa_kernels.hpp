@@ -31,6 +31,9 @@ struct FwdParams {
   int split_len;    // keys per split, a multiple of 128 (>= Nk when unsplit)
   float* o_part;
   float* lse_part;
+  // Head_dim-64 forward: map workgroups in snake order (xcd_item), set by
+  // its launcher for causal launches whose workgroups are all resident.
+  int snake;
 };
 
 // FP8 forward: q, k, v are OCP E4M3 codes (strides in elements = bytes),

@@ -21,6 +21,16 @@
 //     item = i / BH.
 // When R is not a multiple of c, the last window holds ids that name no item
 // (item >= R); those workgroups exit at once.
+//
+// Snake order (snake = true), for causal launches whose workgroups are all
+// resident at once.  Then there is no dynamic dispatch to even out the
+// causal work: an XCD hands its workgroups to its 32 compute units in
+// passes, and with the heaviest items first every pass gives compute unit k
+// an item about as heavy as the previous pass did, so the first units get
+// the heaviest items of every pass.  Reversing every second full pass of 32
+// pairs heavy with light.  A partial last pass keeps its order, so the
+// mapping stays a bijection.  Launches with more workgroups than resident
+// slots keep heaviest-first order, which dynamic dispatch balances.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,12 +51,20 @@ __host__ __device__ inline int64_t xcd_grid(int BH, int R) {
   return static_cast<int64_t>(8) * a * ((R + c - 1) / c);
 }
 
-__host__ __device__ inline XcdItem xcd_item(uint32_t id, int BH, int R) {
+constexpr int kCusPerXcd = 32;  // 256 compute units in 8 XCDs
+
+__host__ __device__ inline XcdItem xcd_item(uint32_t id, int BH, int R, bool snake = false) {
   const int G = (BH & -BH) < 8 ? (BH & -BH) : 8;  // gcd(BH, 8)
   const int a = BH / G;                            // heads per group
   const int c = 8 / G;                             // XCDs per group
   const int x = static_cast<int>(id & 7u);         // XCD
-  const int j = static_cast<int>(id >> 3);         // order on that XCD
+  int j = static_cast<int>(id >> 3);               // order on that XCD
+  if (snake) {
+    const int per_xcd = a * ((R + c - 1) / c);
+    const int pass = j / kCusPerXcd;
+    if ((pass & 1) != 0 && (pass + 1) * kCusPerXcd <= per_xcd)
+      j = pass * kCusPerXcd + (kCusPerXcd - 1 - (j - pass * kCusPerXcd));
+  }
   const int grp = x % G;
   const int xc = x / G;          // XCD's place within its group
   const int w = j / a;           // window

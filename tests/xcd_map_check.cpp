@@ -1,8 +1,9 @@
 // Host-side check of the workgroup -> (head, item) mapping in fa_xcd.hpp,
 // compiled host-only by tests/test_xcd_map.py.
 //
-//   xcd_map_check dump BH R   print "id xcd bh item valid" for every id
-//   xcd_map_check check       exhaustive checks for BH = 1..96, R = 1..80;
+//   xcd_map_check dump BH R [snake]  print "id xcd bh item valid" for every id
+//   xcd_map_check check       exhaustive checks for BH = 1..96, R = 1..80,
+//                             plain and snake order;
 //                             prints "ok <cases>" or the first failure
 #include <cstdio>
 #include <cstdlib>
@@ -17,7 +18,7 @@ static int fail(const char* what, int BH, int R, long id) {
   return 1;
 }
 
-static int check_one(int BH, int R) {
+static int check_one(int BH, int R, bool snake) {
   const int64_t n = xcd_grid(BH, R);
   int G = 1;
   while (G < 8 && BH % (2 * G) == 0) G *= 2;
@@ -27,7 +28,7 @@ static int check_one(int BH, int R) {
   std::vector<int> last_window(8, -1);
   std::vector<long> items_of_xcd(8, 0);
   for (int64_t id = 0; id < n; ++id) {
-    const XcdItem t = xcd_item(static_cast<uint32_t>(id), BH, R);
+    const XcdItem t = xcd_item(static_cast<uint32_t>(id), BH, R, snake);
     if (t.bh < 0 || t.bh >= BH || t.item < 0) return fail("range", BH, R, id);
     if (t.item >= R) {
       if (t.valid) return fail("valid beyond R", BH, R, id);
@@ -39,13 +40,15 @@ static int check_one(int BH, int R) {
     heads_of_xcd[x].insert(t.bh);
     xcds_of_head[t.bh].insert(x);
     ++items_of_xcd[x];
-    // Items reach each XCD window by window (heaviest first).
-    const int win = t.item / c;
-    if (win < last_window[x]) return fail("window order", BH, R, id);
-    last_window[x] = win;
-    // BH a multiple of 8 or BH = 1, 2, 4: the plain i % BH mapping.
-    if ((BH % 8 == 0 || 8 % BH == 0) && (t.bh != id % BH || t.item != id / BH))
-      return fail("not i % BH", BH, R, id);
+    if (!snake) {
+      // Items reach each XCD window by window (heaviest first).
+      const int win = t.item / c;
+      if (win < last_window[x]) return fail("window order", BH, R, id);
+      last_window[x] = win;
+      // BH a multiple of 8 or BH = 1, 2, 4: the plain i % BH mapping.
+      if ((BH % 8 == 0 || 8 % BH == 0) && (t.bh != id % BH || t.item != id / BH))
+        return fail("not i % BH", BH, R, id);
+    }
   }
   for (size_t k = 0; k < seen.size(); ++k)
     if (seen[k] != 1) return fail("item missing", BH, R, static_cast<long>(k));
@@ -73,11 +76,12 @@ static int check_one(int BH, int R) {
 }
 
 int main(int argc, char** argv) {
-  if (argc == 4 && std::strcmp(argv[1], "dump") == 0) {
+  if ((argc == 4 || argc == 5) && std::strcmp(argv[1], "dump") == 0) {
     const int BH = std::atoi(argv[2]), R = std::atoi(argv[3]);
+    const bool snake = argc == 5 && std::strcmp(argv[4], "snake") == 0;
     const int64_t n = xcd_grid(BH, R);
     for (int64_t id = 0; id < n; ++id) {
-      const XcdItem t = xcd_item(static_cast<uint32_t>(id), BH, R);
+      const XcdItem t = xcd_item(static_cast<uint32_t>(id), BH, R, snake);
       std::printf("%ld %ld %d %d %d\n", static_cast<long>(id), static_cast<long>(id % 8), t.bh,
                   t.item, t.valid ? 1 : 0);
     }
@@ -85,9 +89,10 @@ int main(int argc, char** argv) {
   }
   if (argc == 2 && std::strcmp(argv[1], "check") == 0) {
     int cases = 0;
-    for (int BH = 1; BH <= 96; ++BH)
-      for (int R = 1; R <= 80; ++R, ++cases)
-        if (check_one(BH, R)) return 1;
+    for (int snake = 0; snake < 2; ++snake)
+      for (int BH = 1; BH <= 96; ++BH)
+        for (int R = 1; R <= 80; ++R, ++cases)
+          if (check_one(BH, R, snake != 0)) return 1;
     std::printf("ok %d\n", cases);
     return 0;
   }
