@@ -107,7 +107,7 @@ void fwd_kernel(FwdParams p) {
   constexpr bool PAIRED = CAUSAL && SPLIT;
   const int slots = PAIRED ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
   const int BH = p.B * p.H;
-  const XcdItem wg = xcd_item(blockIdx.x, BH, slots * p.num_splits);
+  const XcdItem wg = xcd_item(blockIdx.x, BH, slots * p.num_splits, p.snake != 0);
   if (!wg.valid) return;
   poison_lds(Ks0, Ks1, Vs0, Vs1);
   const int bh = wg.bh;
@@ -451,6 +451,11 @@ static hipError_t launch_fwd_nw(const FwdParams& p_in, hipStream_t s) {
   // Causal split launches run blocks i and n-1-i in one workgroup.
   const int slots = CAUSAL && SPLIT ? (p.num_qblocks + 1) / 2 : p.num_qblocks;
   const int64_t blocks = xcd_grid(p.B * p.H, slots * p.num_splits);
+  // Resident workgroups per compute unit (two waves per SIMD at head_dim
+  // 128): two 4-wave ones, one 8-wave one.  A causal, unpaired grid that fits
+  // runs at once, so its blocks go out in snake order (xcd_item).
+  const int64_t resident = 256 * (NW == 4 ? 2 : 1);
+  p.snake = CAUSAL && !SPLIT && p.num_splits == 1 && blocks <= resident ? 1 : 0;
   hipLaunchKernelGGL((fwd_kernel<T, D, NW, CAUSAL, SPLIT>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * NW), 0, s, p);
   return hipGetLastError();

@@ -31,8 +31,8 @@ struct FwdParams {
   int split_len;    // keys per split, a multiple of 128 (>= Nk when unsplit)
   float* o_part;
   float* lse_part;
-  // Head_dim-64 forward: map workgroups in snake order (xcd_item), set by
-  // its launcher for causal launches whose workgroups are all resident.
+  // Map workgroups in snake order (xcd_item): set by the forward launchers
+  // for causal launches whose workgroups are all resident at once.
   int snake;
 };
 
