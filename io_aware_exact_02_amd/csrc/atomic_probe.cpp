@@ -79,15 +79,15 @@ float time_mode(void* acc, size_t bytes, int reps) {
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1.0f;
   if (hipMemset(acc, 0, bytes) != hipSuccess) return -1.0f;
   hipLaunchKernelGGL(probe<MODE>, dim3(grid), dim3(256), 0, 0, acc);  // warm-up
-  if (hipDeviceSynchronize() != hipSuccess) return -1.0f;
-  hipEventRecord(e0, 0);
+  if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) return -1.0f;
+  if (hipEventRecord(e0, 0) != hipSuccess) return -1.0f;
   for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(probe<MODE>, dim3(grid), dim3(256), 0, 0, acc);
-  hipEventRecord(e1, 0);
-  if (hipEventSynchronize(e1) != hipSuccess) return -1.0f;
+  if (hipGetLastError() != hipSuccess || hipEventRecord(e1, 0) != hipSuccess ||
+      hipEventSynchronize(e1) != hipSuccess)
+    return -1.0f;
   float ms = 0.0f;
-  hipEventElapsedTime(&ms, e0, e1);
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  const bool ok = hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+  if (hipEventDestroy(e0) != hipSuccess || hipEventDestroy(e1) != hipSuccess || !ok) return -1.0f;
   return ms / reps;
 }
 
@@ -107,8 +107,8 @@ int main() {
   const float t32 = time_mode<0>(acc, bytes, reps);
   const float t64 = time_mode<1>(acc, bytes, reps);
   const float tf = time_mode<2>(acc, bytes, reps);
-  hipFree(acc);
-  if (t32 <= 0.0f || t64 <= 0.0f || tf <= 0.0f) {
+  const bool freed = hipFree(acc) == hipSuccess;
+  if (t32 <= 0.0f || t64 <= 0.0f || tf <= 0.0f || !freed) {
     std::printf("{\"error\": \"HIP call failed\"}\n");
     return 1;
   }

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(FwdOccupancy<D, NW, CAUSAL>::value)))
 void fwd_kernel(FwdParams p) {
   using Cfg = FwdCfg<D, NW, SPLIT>;
-  constexpr int BR = Cfg::BR, BC = Cfg::BC, THREADS = Cfg::THREADS;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC;
   constexpr int CPR = Cfg::CPR, NCH = Cfg::NCH;
   constexpr int KC = D / 16;   // 16-wide k slices of Q K^T
   constexpr int DB = D / 32;   // 32-wide d blocks of O
