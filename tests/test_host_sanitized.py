@@ -19,8 +19,10 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "io_aware_exact_02_amd", "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-OBJS = [os.path.join(ROOT, "_build", f + ".o")
-        for f in ("fa_fwd", "fa_fwd64", "fa_fwd8", "fa_bwd", "fa_merge")]
+from io_aware_exact_02_amd import build as _build  # noqa: E402  (source list only)
+
+OBJS = [os.path.join(ROOT, "_build", f.rsplit(".", 1)[0] + ".o")
+        for f in _build.SOURCES if f != "fa_api.cpp"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 # Sanitizers on the host half only (the device half is never sanitized).
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
