@@ -197,6 +197,29 @@ def test_head_counts_off_the_xcd_grid(B, H, D, causal):
     assert_forward(got, O, LSE, what + " split 3")
 
 
+@pytest.mark.parametrize("B,H,N,D", [(4, 8, 4096, 64), (2, 8, 4096, 64), (4, 16, 900, 128)])
+def test_snake_order_grids(B, H, N, D):
+    """Causal grids whose workgroups are all resident at once get their
+    blocks in snake order (every second pass of 32 reversed): the 8-wave and
+    4-wave head_dim-64 forwards and the 4-wave head_dim-128 one.  O, LSE and
+    dQ at 48 sampled rows of every head, dK and dV in full on one head."""
+    what = f"snake B={B} H={H} N={N} D={D}"
+    _say("case", what)
+    inp = random_qkv(B, N, H, D, "bf16", seed=7950 + N + D)
+    got = gpu_forward_backward(inp, True)
+    rows = sample_rows(N, 48, seed=N + D)
+    for b in range(B):
+        for h in range(H):
+            r = oa.attention_rows(inp["q"], inp["k"], inp["v"], inp["do"], b, h, rows, causal=True)
+            sub = {"O": got["O"][b, rows, h], "LSE": got["LSE"][b, h, rows]}
+            assert_forward(sub, r["O"], r["LSE"], f"{what} b{b} h{h}")
+            assert_grad("dQ", got["dQ"][b, rows, h], r["dQ"], f"{what} b{b} h{h}")
+    _, dK, dV = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=True,
+                                      heads=[(B - 1, H - 1)])
+    assert_grad("dK", got["dK"][B - 1, :, H - 1], dK[B - 1, :, H - 1], what)
+    assert_grad("dV", got["dV"][B - 1, :, H - 1], dV[B - 1, :, H - 1], what)
+
+
 # ------------------------------------------------------------ the five configs
 
 def test_config_c1():
