@@ -787,8 +787,8 @@ def main(argv=None):
         "fp8_forward": fp8,
         "head_shard_c5_of_8": shard,
         "split_kv": splits,
-        # The marketing name can be empty where the driver's id table is not
-        # installed; the architecture name is always there.
+        # The marketing name can be empty where libdrm's amdgpu.ids table is
+        # not installed; the architecture name is always there.
         "device": {"name": torch.cuda.get_device_properties(0).name
                    or getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
