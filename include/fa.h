@@ -155,16 +155,18 @@ int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
  * fa_bwd_workspace_bytes -- size of the scratch fa_bwd needs: the row vector
  * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
  * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]
- * (fp32), one dQ bound per head [B*H] (fp32), and -- for launches with fewer than 512
- * key blocks of 256 (D = 64) or 128 (D = 128) keys, which a causal mask
- * splits into two query segments -- partial dK and dV sums [2, B, H, N, D]
- * (fp32) each; every part rounded up to 256 bytes.  O(N*D) per head; no N*N
- * term.  Returns 0 for invalid sizes.
+ * (fp32), one dQ bound per head [B*H] (fp32), and -- for launches with
+ * fewer than 512 key blocks of 256 (D = 64) or 128 (D = 128) keys, whose
+ * query range a causal mask splits into S segments -- partial dK and dV
+ * sums [S, B, H, N, D] (fp32) each, with S = min(8, ceil(512 / key blocks),
+ * ceil(N / 64)) (no partials when S = 1); every part rounded up to 256
+ * bytes.  O(N*D) per head; no N*N term.  Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 
 /* Workspace of fa_bwd_qk: as above with Dvec and the dQ accumulator over Nq
- * rows and the maxima over ceil(max(Nq, Nk) / 16) blocks. */
+ * rows, the maxima over ceil(max(Nq, Nk) / 16) blocks, and the partial sums
+ * [S, B, H, Nk, D] with S from the key blocks of Nk and ceil(Nq / 64). */
 size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
 
 /*

@@ -74,7 +74,7 @@ BwdWorkspace bwd_workspace(int B, int H, int Nq, int Nk, int D) {
   const size_t heads = static_cast<size_t>(B) * H;
   const size_t rows = heads * Nq;
   const size_t nmax = static_cast<size_t>(Nq > Nk ? Nq : Nk);
-  const int segs = fa::bwd_segments(B, H, Nk, D, true);
+  const int segs = fa::bwd_segments(B, H, Nq, Nk, D, true);
   const size_t part_bytes = segs > 1 ? static_cast<size_t>(segs) * heads * Nk * D * sizeof(float) : 0;
   BwdWorkspace w{};
   w.dvec = 0;

@@ -649,15 +649,27 @@ struct BwdShape {
   static constexpr int BKV = BwdCfg<D, NW, BQ>::BKV;
 };
 
-// Query segments per key block (BwdParams nseg): 2 for causal launches with
-// fewer than two key blocks per compute unit (256 on MI355X), where the
-// heaviest key block holds about twice the average work; 1 otherwise.
-// (One GPU's share of B1 H16 N16384 D64 under 8-way head sharding, 128 key
-// blocks: forward + backward 0.73 -> 0.49 ms.)
-int bwd_segments(int B, int H, int Nk, int D, bool causal) {
+// Query segments per key block (BwdParams nseg).  Causal launches with
+// fewer than 512 key blocks (two per compute unit on MI355X) get enough
+// segments for about 512 workgroups, at most 8 and at most the 64-row query
+// tiles of the heaviest key block; every other launch gets 1.  The heaviest
+// key block of a causal launch holds about twice the average work, and a
+// launch of few workgroups leaves compute units idle.  Measured on the
+// backward (in-process A/B on one box): B1 H1 N16384 D64 (64 key blocks,
+// 8 segments) 0.368 -> 0.150 ms; B1 H2 N16384 D64 (128, 4) 0.373 ->
+// 0.238 ms; B1 H1 N16384 D128 (128, 4) 0.555 -> 0.383 ms.  256 key blocks
+// keep 2 segments (4 were 4-9% slower), and non-causal launches, whose
+// workgroups all carry equal work, keep 1.
+int bwd_segments(int B, int H, int Nq, int Nk, int D, bool causal) {
   const int bkv = D == 64 ? BwdShape<64>::BKV : BwdShape<128>::BKV;
   const int64_t blocks = static_cast<int64_t>(B) * H * ((Nk + bkv - 1) / bkv);
-  return causal && blocks < 2 * 256 ? 2 : 1;
+  if (!causal || blocks >= 2 * 256 || blocks <= 0) return 1;
+  int64_t s = (2 * 256 + blocks - 1) / blocks;
+  const int bq = D == 64 ? BwdShape<64>::BQ : BwdShape<128>::BQ;
+  const int64_t tiles = (static_cast<int64_t>(Nq) + bq - 1) / bq;
+  if (s > 8) s = 8;
+  if (s > tiles) s = tiles;
+  return s > 1 ? static_cast<int>(s) : 1;
 }
 
 // ------------------------------------------------------------------ kernel 2b
@@ -731,7 +743,7 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   constexpr int NW = Sh::NW;
   BwdParams p = p_in;
   p.num_kblocks = (p.Nk + Sh::BKV - 1) / Sh::BKV;
-  p.nseg = bwd_segments(p.B, p.H, p.Nk, D, CAUSAL);
+  p.nseg = bwd_segments(p.B, p.H, p.N, p.Nk, D, CAUSAL);
   constexpr int RPB = 256 / (D / 8);
   p.npart = (max(p.N, p.Nk) + RPB - 1) / RPB;
   const dim3 row_grid(static_cast<unsigned>(p.npart), static_cast<unsigned>(p.B * p.H));

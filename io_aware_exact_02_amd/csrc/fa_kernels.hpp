@@ -106,9 +106,9 @@ hipError_t launch_fwd64(const FwdParams& p, int dtype, bool causal, hipStream_t 
 // stages: bit 0 preprocess, bit 1 dK/dV (+ dQ accumulation), bit 2 dQ conversion.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int D, int causal, unsigned stages,
                       hipStream_t s);
-// Query segments per key block of the dK/dV kernel for a launch (1 or 2);
+// Query segments per key block of the dK/dV kernel for a launch (1 to 8);
 // the backward workspace holds partial dK, dV sums for that many.
-int bwd_segments(int B, int H, int Nk, int D, bool causal);
+int bwd_segments(int B, int H, int Nq, int Nk, int D, bool causal);
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_split_merge(const SplitMergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_fwd8(const Fwd8Params& p, int out_dtype, int D, int causal, hipStream_t s);

@@ -51,13 +51,15 @@ def test_workspace_bytes_is_linear_in_n():
 
     # Dvec, the int32 dQ accumulator, three maxima per 16-row block, one
     # fixed-point bound per head, and -- for launches with fewer than 512 key
-    # blocks (256 keys at head_dim 64, 128 at head_dim 128), which a causal
-    # mask splits into two query segments -- two fp32 partial dK and dV
-    # sums: O(N*D) per head, no N*N term.
+    # blocks (256 keys at head_dim 64, 128 at head_dim 128), whose query
+    # range a causal mask splits into S = min(8, ceil(512 / blocks),
+    # ceil(N / 64)) segments -- S fp32 partial dK and dV sums: O(N*D) per
+    # head, no N*N term.
     def want_bytes(B, H, N, D):
         heads, rows = B * H, B * H * N
         bkv = 256 if D == 64 else 128
-        segs = 2 if heads * ((N + bkv - 1) // bkv) < 512 else 1
+        blocks = heads * ((N + bkv - 1) // bkv)
+        segs = min(8, -(-512 // blocks), -(-N // 64)) if blocks < 512 else 1
         part = 2 * a256(4 * segs * heads * N * D) if segs > 1 else 0
         return (a256(4 * rows) + a256(4 * rows * D)
                 + a256(4 * 3 * heads * ((N + 15) // 16)) + a256(4 * heads) + part)

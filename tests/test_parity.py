@@ -220,6 +220,28 @@ def test_snake_order_grids(B, H, N, D):
     assert_grad("dV", got["dV"][B - 1, :, H - 1], dV[B - 1, :, H - 1], what)
 
 
+@pytest.mark.parametrize("B,H,N,D,segs", [
+    (1, 1, 4096, 64, 8),     # 16 key blocks
+    (1, 7, 4000, 64, 5),     # 112 key blocks, ragged tail
+    (1, 12, 4096, 64, 3),    # 192 key blocks
+    (3, 2, 200, 64, 4),      # 6 key blocks, capped by the 4 query tiles
+    (1, 2, 2048, 128, 8),    # 32 key blocks
+    (1, 8, 2048, 128, 4),    # 128 key blocks
+])
+def test_query_segment_counts(B, H, N, D, segs):
+    """Causal launches with fewer than 512 key blocks split each key block's
+    query tiles over S workgroups (S = min(8, ceil(512 / blocks), query
+    tiles)) and add their fp32 partial dK, dV in segment order.  Every
+    output against the oracle, in full, at S = 3, 4, 5 and 8."""
+    what = f"segments B={B} H={H} N={N} D={D}"
+    bkv = 256 if D == 64 else 128
+    blocks = B * H * -(-N // bkv)
+    assert min(8, -(-512 // blocks), -(-N // 64)) == segs, what
+    _say("case", what, "S =", segs)
+    inp = random_qkv(B, N, H, D, "bf16", seed=8100 + N + H)
+    check_full(inp, True, what=what)
+
+
 # ------------------------------------------------------------ the five configs
 
 def test_config_c1():
