@@ -166,8 +166,17 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 
 /* Workspace of fa_bwd_qk: as above with Dvec and the dQ accumulator over Nq
  * rows, the maxima over ceil(max(Nq, Nk) / 16) blocks, and the partial sums
- * [S, B, H, Nk, D] with S from the key blocks of Nk and ceil(Nq / 64). */
+ * [S, B, H, Nk, D] with S from the key blocks of Nk and ceil(Nq / 64).
+ * Like fa_bwd_workspace_bytes, it is the size for a causal launch, which
+ * serves either mask. */
 size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
+
+/* The workspace one mask needs (causal 0 or 1): fa_bwd_qk_workspace_bytes
+ * for causal = 1; without the partial dK, dV sums for causal = 0, since
+ * non-causal launches run one query segment.  The partial sums are the last
+ * part of the layout, so a buffer of this size and one of the causal size
+ * are used identically below it.  Returns 0 for invalid sizes or causal. */
+size_t fa_bwd_qk_workspace_bytes_for(int B, int H, int Nq, int Nk, int D, int causal);
 
 /*
  * fa_bwd -- attention backward by recomputation.
@@ -179,8 +188,10 @@ size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
  *                     packed dqkv tensor but must not overlap each other or
  *                     any input.
  *   workspace       : device buffer of at least
- *                     fa_bwd_workspace_bytes(B, H, N, D) bytes, 256-byte
- *                     aligned; contents undefined on entry and on exit.
+ *                     fa_bwd_qk_workspace_bytes_for(B, H, N, N, D, causal)
+ *                     bytes (fa_bwd_workspace_bytes(B, H, N, D) serves
+ *                     either mask), 256-byte aligned; contents undefined on
+ *                     entry and on exit.
  * Three kernels are enqueued on `stream`: the Dvec preprocess (which also
  * clears the dQ accumulator and takes the largest |dO_i|, |K| element
  * and |V_j| per head, |.| the Euclidean norm of a row), the K/V-block-

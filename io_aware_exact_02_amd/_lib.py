@@ -20,7 +20,8 @@ FA_F16, FA_BF16 = 0, 1
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_qk", "fa_fwd_split", "fa_fwd_split_workspace_bytes",
            "fa_fwd_split_count", "fa_fwd_fp8", "fa_bwd", "fa_bwd_stages", "fa_bwd_qk",
-           "fa_bwd_workspace_bytes", "fa_bwd_qk_workspace_bytes", "fa_bwd_noalloc",
+           "fa_bwd_workspace_bytes", "fa_bwd_qk_workspace_bytes",
+           "fa_bwd_qk_workspace_bytes_for", "fa_bwd_noalloc",
            "fa_bwd_noalloc_max_bytes", "fa_merge", "fa_status_str", "fa_version")
 STAGE_PREPROCESS, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 
@@ -94,6 +95,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa_bwd_noalloc_max_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_qk_workspace_bytes_for.argtypes = [i, i, i, i, i, i]
+    lib.fa_bwd_qk_workspace_bytes_for.restype = ctypes.c_size_t
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
                                ctypes.POINTER(FwdStrides), vp]
     lib.fa_fwd_fp8.restype = i

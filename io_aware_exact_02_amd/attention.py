@@ -215,9 +215,15 @@ def fwd_fp8(q, k, v, descale_q=None, descale_k=None, descale_v=None, causal: boo
     return out, lse
 
 
-def workspace_bytes(B: int, H: int, N: int, D: int, Nk: int | None = None) -> int:
-    """Backward workspace for N query rows against Nk (default N) keys."""
-    return int(_lib.load().fa_bwd_qk_workspace_bytes(B, H, N, N if Nk is None else Nk, D))
+def workspace_bytes(B: int, H: int, N: int, D: int, Nk: int | None = None,
+                    causal: bool | None = None) -> int:
+    """Backward workspace for N query rows against Nk (default N) keys: the
+    size one mask needs, or (causal=None) the size that serves either."""
+    lib = _lib.load()
+    nk = N if Nk is None else Nk
+    if causal is None:
+        return int(lib.fa_bwd_qk_workspace_bytes(B, H, N, nk, D))
+    return int(lib.fa_bwd_qk_workspace_bytes_for(B, H, N, nk, D, int(bool(causal))))
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
@@ -244,7 +250,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale=None,
         dv = torch.empty((B, Nk, H, D), dtype=q.dtype, device=q.device)
     _check_inputs(q, dq)
     _check_inputs(k, dk, dv)
-    need = lib.fa_bwd_qk_workspace_bytes(B, H, N, Nk, D)
+    need = lib.fa_bwd_qk_workspace_bytes_for(B, H, N, Nk, D, int(bool(causal)))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = _lib.BwdStrides(*(_stride3(t) for t in (q, k, v, o, dout, dq, dk, dv)))

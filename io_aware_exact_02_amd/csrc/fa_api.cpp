@@ -65,16 +65,17 @@ namespace {
 // boundary: Dvec [B, H, Nq] fp32 | dQ accumulator [B, H, Nq, D] int32 |
 // bound maxima [B*H, 3, ceil(max(Nq, Nk) / 16)] fp32 | dQ bound [B*H] fp32 |
 // partial dK and dV sums [S, B*H, Nk, D] fp32 each, S the query segments of
-// a causal launch of this size (none when S = 1; sized for causal, so that
-// the size does not depend on the mask).
+// the launch (none when S = 1, e.g. every non-causal launch).  The partial
+// sums come last, so the other offsets do not depend on the mask, and the
+// causal size serves either mask.
 struct BwdWorkspace {
   size_t dvec, dq, part, unit, dk_part, dv_part, total;
 };
-BwdWorkspace bwd_workspace(int B, int H, int Nq, int Nk, int D) {
+BwdWorkspace bwd_workspace(int B, int H, int Nq, int Nk, int D, bool causal) {
   const size_t heads = static_cast<size_t>(B) * H;
   const size_t rows = heads * Nq;
   const size_t nmax = static_cast<size_t>(Nq > Nk ? Nq : Nk);
-  const int segs = fa::bwd_segments(B, H, Nq, Nk, D, true);
+  const int segs = fa::bwd_segments(B, H, Nq, Nk, D, causal);
   const size_t part_bytes = segs > 1 ? static_cast<size_t>(segs) * heads * Nk * D * sizeof(float) : 0;
   BwdWorkspace w{};
   w.dvec = 0;
@@ -217,9 +218,10 @@ int make_bwd_params(fa::BwdParams& p, const void* q, const void* k, const void* 
 }
 
 // Points the parameter block's scratch at a workspace of at least
-// bwd_workspace(B, H, Nq, Nk, D).total bytes, 256-byte aligned.
-void set_bwd_workspace(fa::BwdParams& p, void* workspace, int B, int H, int Nq, int Nk, int D) {
-  const BwdWorkspace w = bwd_workspace(B, H, Nq, Nk, D);
+// bwd_workspace(B, H, Nq, Nk, D, causal).total bytes, 256-byte aligned.
+void set_bwd_workspace(fa::BwdParams& p, void* workspace, int B, int H, int Nq, int Nk, int D,
+                       bool causal) {
+  const BwdWorkspace w = bwd_workspace(B, H, Nq, Nk, D, causal);
   char* ws = static_cast<char*>(workspace);
   p.dvec = reinterpret_cast<float*>(ws + w.dvec);
   p.dq_fix = reinterpret_cast<int32_t*>(ws + w.dq);
@@ -397,8 +399,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D) {
+  return fa_bwd_qk_workspace_bytes_for(B, H, Nq, Nk, D, 1);
+}
+
+size_t fa_bwd_qk_workspace_bytes_for(int B, int H, int Nq, int Nk, int D, int causal) {
   if (rows_of(B, H, Nq) < 0 || rows_of(B, H, Nk) < 0 || (D != 64 && D != 128)) return 0;
-  return bwd_workspace(B, H, Nq, Nk, D).total;
+  if (causal != 0 && causal != 1) return 0;
+  return bwd_workspace(B, H, Nq, Nk, D, causal != 0).total;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D) {
@@ -415,9 +422,10 @@ int fa_bwd_qk(const void* q, const void* k, const void* v, const void* o, const 
   int st = make_bwd_params(p, q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, causal, scale,
                            dtype, strides);
   if (st != FA_OK) return st;
-  if (workspace_bytes < fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_qk_workspace_bytes_for(B, H, Nq, Nk, D, causal))
+    return FA_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FA_ERR_UNSUPPORTED;
-  set_bwd_workspace(p, workspace, B, H, Nq, Nk, D);
+  set_bwd_workspace(p, workspace, B, H, Nq, Nk, D, causal != 0);
   const hipError_t e = fa::launch_bwd(p, dtype, D, causal, stages, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -432,10 +440,11 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   int st = make_bwd_params(p, q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, D, causal, scale,
                            dtype, strides);
   if (st != FA_OK) return st;
-  if (fa_bwd_qk_workspace_bytes(B, H, Nq, Nk, D) > kNoallocScratchBytes) return FA_ERR_TOO_LARGE;
+  if (fa_bwd_qk_workspace_bytes_for(B, H, Nq, Nk, D, causal) > kNoallocScratchBytes)
+    return FA_ERR_TOO_LARGE;
   void* scratch = nullptr;
   if ((st = noalloc_scratch(&scratch)) != FA_OK) return st;
-  set_bwd_workspace(p, scratch, B, H, Nq, Nk, D);
+  set_bwd_workspace(p, scratch, B, H, Nq, Nk, D, causal != 0);
   const hipError_t e = fa::launch_bwd(p, dtype, D, causal, FA_STAGE_ALL, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

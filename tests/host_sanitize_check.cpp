@@ -44,6 +44,11 @@ int main() {
   ++checks;
   if (fa_bwd_workspace_bytes(-1, H, N, D) != 0 || fa_bwd_qk_workspace_bytes(B, H, N, N, 96) != 0)
     failed = 1;
+  ++checks;  // the causal size serves either mask; causal must be 0 or 1
+  if (fa_bwd_qk_workspace_bytes_for(B, H, N, N, D, 1) != fa_bwd_workspace_bytes(B, H, N, D) ||
+      fa_bwd_qk_workspace_bytes_for(B, H, N, N, D, 0) > fa_bwd_workspace_bytes(B, H, N, D) ||
+      fa_bwd_qk_workspace_bytes_for(B, H, N, N, D, 2) != 0)
+    failed = 1;
   ++checks;
   if (fa_fwd_split_count(B, H, N, N, D, 1) < 1) failed = 1;
 
@@ -73,6 +78,10 @@ int main() {
   expect(fa_bwd(P, P, P, P, P, F, P, P, P, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, P, ws - 1,
                 nullptr),
          FA_ERR_INVALID_ARG, "fa_bwd small workspace");
+  const size_t ws_nc = fa_bwd_qk_workspace_bytes_for(B, H, N, N, D, 0);
+  expect(fa_bwd(P, P, P, P, P, F, P, P, P, B, H, N, D, 0, 0.125f, FA_BF16, nullptr, P, ws_nc - 1,
+                nullptr),
+         FA_ERR_INVALID_ARG, "fa_bwd small non-causal workspace");
   expect(fa_bwd(P, P, P, P, P, nullptr, P, P, P, B, H, N, D, 1, 0.125f, FA_BF16, nullptr, P, ws,
                 nullptr),
          FA_ERR_INVALID_ARG, "fa_bwd null lse");

@@ -126,8 +126,12 @@ def test_fwd_rejects_bad_strides():
 
 
 def test_bwd_rejects_before_launch():
-    need = _lib.load().fa_bwd_workspace_bytes(1, 1, 128, 64)
-    assert _bwd(ws_bytes=need - 1) == _lib.FA_ERR_INVALID_ARG
+    lib = _lib.load()
+    need = lib.fa_bwd_workspace_bytes(1, 1, 128, 64)   # the causal size
+    assert _bwd(ws_bytes=need - 1, causal=1) == _lib.FA_ERR_INVALID_ARG
+    need_nc = lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 128, 64, 0)
+    assert need_nc < need
+    assert _bwd(ws_bytes=need_nc - 1) == _lib.FA_ERR_INVALID_ARG
     assert _bwd(ws=None) == _lib.FA_ERR_INVALID_ARG
     assert _bwd(ws=P + 16) == _lib.FA_ERR_UNSUPPORTED       # workspace needs 256 B alignment
     for i in range(9):
@@ -199,7 +203,15 @@ def test_unequal_length_entry_points_reject_before_launch():
         return lib.fa_bwd_qk(*([P] * 9), a["B"], a["H"], Nq, Nk, a["D"], a["causal"],
                              a["scale"], a["dtype"], None, P, ws_bytes, stages, None)
 
-    assert bwd_qk(ws_bytes=need - 1) == _lib.FA_ERR_INVALID_ARG
+    assert bwd_qk(ws_bytes=need - 1, causal=1) == _lib.FA_ERR_INVALID_ARG
+    # A non-causal launch runs one query segment: its workspace has no partial
+    # sums, and the causal size serves it too.
+    need_nc = lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 0)
+    assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 1) == need
+    assert need_nc == need - 2 * a256(4 * 2 * 256 * 64)
+    assert bwd_qk(ws_bytes=need_nc - 1, causal=0) == _lib.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 2) == 0
+    assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 0, 256, 64, 0) == 0
     assert bwd_qk(Nk=0) == _lib.FA_ERR_INVALID_ARG
     assert bwd_qk(stages=0) == _lib.FA_ERR_INVALID_ARG
     assert bwd_qk(stages=16) == _lib.FA_ERR_INVALID_ARG
