@@ -156,11 +156,14 @@ int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
  * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
  * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]
  * (fp32), one dQ bound per head [B*H] (fp32), and -- for launches with
- * fewer than 512 key blocks of 256 (D = 64) or 128 (D = 128) keys, whose
- * query range a causal mask splits into S segments -- partial dK and dV
- * sums [S, B, H, N, D] (fp32) each, with S = min(8, ceil(512 / key blocks),
- * ceil(N / 64)) (no partials when S = 1); every part rounded up to 256
- * bytes.  O(N*D) per head; no N*N term.  Returns 0 for invalid sizes.
+ * few key blocks of 256 (D = 64) or 128 (D = 128) keys, whose query range is
+ * split into S segments -- partial dK and dV sums [S, B, H, N, D] (fp32)
+ * each.  S = min(8, ceil(512 / key blocks), ceil(N / 64)) for a causal
+ * launch with fewer than 512 key blocks, min(8, ceil(256 / key blocks),
+ * ceil(N / 64)) for a non-causal one with at most 128, else 1 (no partials
+ * when S = 1).  This size is the causal one, which serves either mask.
+ * Every part is rounded up to 256 bytes.  O(N*D) per head; no N*N term.
+ * Returns 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 
@@ -172,8 +175,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);
 
 /* The workspace one mask needs (causal 0 or 1): fa_bwd_qk_workspace_bytes
- * for causal = 1; without the partial dK, dV sums for causal = 0, since
- * non-causal launches run one query segment.  The partial sums are the last
+ * for causal = 1; for causal = 0, the partial dK, dV sums of the non-causal
+ * segment count (none above 128 key blocks).  The partial sums are the last
  * part of the layout, so a buffer of this size and one of the causal size
  * are used identically below it.  Returns 0 for invalid sizes or causal. */
 size_t fa_bwd_qk_workspace_bytes_for(int B, int H, int Nq, int Nk, int D, int causal);
@@ -197,10 +200,11 @@ size_t fa_bwd_qk_workspace_bytes_for(int B, int H, int Nq, int Nk, int D, int ca
  * and |V_j| per head, |.| the Euclidean norm of a row), the K/V-block-
  * parallel dK/dV kernel that accumulates dQ with 32-bit integer atomics in
  * units of B / 2^30, B = 4 max|K| max|dO_i| max|V_j| per (batch, head) --
- * a bound on any partial sum of dS K -- and the dQ conversion (narrow
- * causal launches add a fourth, which sums the partial dK, dV of the query
- * segments).  The integer sum is exact, so dq is bitwise reproducible;
- * each key block's contribution is rounded to the nearest unit.  B is
+ * a bound on any partial sum of dS K -- and the dQ conversion.  Narrow
+ * launches (causal below 512 key blocks, non-causal at 128 or fewer) add a
+ * fourth, which sums the partial dK, dV of the query segments.  The integer
+ * dQ sum is exact, so dq is bitwise reproducible; each key block's
+ * contribution is rounded to the nearest unit.  B is
  * raised to at least 2^-96 (the scale 2^30 / B stays finite); heads whose
  * bound is not finite (non-finite inputs) get dq = NaN.
  */

@@ -17,8 +17,8 @@
 //      query tiles; dQ contributions are added to the accumulator with
 //      integer atomics (fixed point, see below);
 //   3. dQ conversion: scale, round to the input type, strided store.
-// Causal launches with few key blocks split each key block's query tiles
-// over two workgroups (query segments); a small kernel then adds their fp32
+// Launches with few key blocks split each key block's query tiles over
+// several workgroups (query segments); a small kernel then adds their fp32
 // partial dK, dV sums in a fixed order.
 //
 // dQ accumulator.  Each dQ element receives one partial sum per key block,
@@ -174,8 +174,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 // block are cut into nseg contiguous segments, each run by its own
 // workgroup, which writes fp32 partial dK, dV sums to the workspace instead
 // of dk, dv; bwd_dkdv_merge_kernel adds the nseg partials in segment order.
-// This evens out causal launches with few key blocks, where the first key
-// block's query range is the whole sequence and the last one's one tile.
+// This fills the device in launches with few key blocks, and evens out
+// causal ones, where the first key block's query range is the whole
+// sequence and the last one's one tile.
 template <int D, int NW, int BQ_>
 struct BwdCfg {
   static constexpr int BKV = 32 * NW;   // keys per workgroup
@@ -649,22 +650,27 @@ struct BwdShape {
   static constexpr int BKV = BwdCfg<D, NW, BQ>::BKV;
 };
 
-// Query segments per key block (BwdParams nseg).  Causal launches with
-// fewer than 512 key blocks (two per compute unit on MI355X) get enough
-// segments for about 512 workgroups, at most 8 and at most the 64-row query
-// tiles of the heaviest key block; every other launch gets 1.  The heaviest
-// key block of a causal launch holds about twice the average work, and a
-// launch of few workgroups leaves compute units idle.  Measured on the
-// backward (in-process A/B on one box): B1 H1 N16384 D64 (64 key blocks,
-// 8 segments) 0.368 -> 0.150 ms; B1 H2 N16384 D64 (128, 4) 0.373 ->
-// 0.238 ms; B1 H1 N16384 D128 (128, 4) 0.555 -> 0.383 ms.  256 key blocks
-// keep 2 segments (4 were 4-9% slower), and non-causal launches, whose
-// workgroups all carry equal work, keep 1.
+// Query segments per key block (BwdParams nseg): enough for about 512
+// workgroups in causal launches with fewer than 512 key blocks, and about 256
+// in non-causal launches with at most 128 key blocks; at most 8, and at most
+// the 64-row query tiles of the heaviest key block; 1 for every other launch.
+// The heaviest key block of a causal launch holds about twice the average
+// work, and a launch of few workgroups leaves compute units idle.  Measured
+// on the backward (in-process A/B on one box): causal B1 H1 N16384 D64 (64
+// key blocks, 8 segments) 0.368 -> 0.150 ms, B1 H2 N16384 D64 (128, 4)
+// 0.373 -> 0.238 ms, B1 H1 N16384 D128 (128, 4) 0.555 -> 0.383 ms;
+// non-causal B1 H2 N16384 D64 (128, 2) 0.577 -> 0.375 ms, B1 H1 N16384 D128
+// (128, 2) 1.074 -> 0.671 ms.  Causal launches of 256 key blocks keep 2
+// segments (4 were 4-9% slower), and non-causal ones of 192 (B2 H12 N2048
+// D64) keep 1 (2 were 20% slower: the partial sums cost more than the
+// quarter of the compute units they would fill).
 int bwd_segments(int B, int H, int Nq, int Nk, int D, bool causal) {
   const int bkv = D == 64 ? BwdShape<64>::BKV : BwdShape<128>::BKV;
   const int64_t blocks = static_cast<int64_t>(B) * H * ((Nk + bkv - 1) / bkv);
-  if (!causal || blocks >= 2 * 256 || blocks <= 0) return 1;
-  int64_t s = (2 * 256 + blocks - 1) / blocks;
+  if (blocks <= 0) return 1;
+  if (causal ? blocks >= 2 * 256 : blocks > 128) return 1;
+  const int64_t target = causal ? 2 * 256 : 256;
+  int64_t s = (target + blocks - 1) / blocks;
   const int bq = D == 64 ? BwdShape<64>::BQ : BwdShape<128>::BQ;
   const int64_t tiles = (static_cast<int64_t>(Nq) + bq - 1) / bq;
   if (s > 8) s = 8;
@@ -754,8 +760,8 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   }
   if (stages & 2u) {
     const int64_t blocks = xcd_grid(p.B * p.H, p.num_kblocks * p.nseg);
-    if (CAUSAL && p.nseg > 1) {  // only causal launches use query segments
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, CAUSAL>),
+    if (p.nseg > 1) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, true>),
                          dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
     } else {
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, false>),

@@ -130,7 +130,7 @@ def test_bwd_rejects_before_launch():
     need = lib.fa_bwd_workspace_bytes(1, 1, 128, 64)   # the causal size
     assert _bwd(ws_bytes=need - 1, causal=1) == _lib.FA_ERR_INVALID_ARG
     need_nc = lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 128, 64, 0)
-    assert need_nc < need
+    assert need_nc <= need
     assert _bwd(ws_bytes=need_nc - 1) == _lib.FA_ERR_INVALID_ARG
     assert _bwd(ws=None) == _lib.FA_ERR_INVALID_ARG
     assert _bwd(ws=P + 16) == _lib.FA_ERR_UNSUPPORTED       # workspace needs 256 B alignment
@@ -204,12 +204,17 @@ def test_unequal_length_entry_points_reject_before_launch():
                              a["scale"], a["dtype"], None, P, ws_bytes, stages, None)
 
     assert bwd_qk(ws_bytes=need - 1, causal=1) == _lib.FA_ERR_INVALID_ARG
-    # A non-causal launch runs one query segment: its workspace has no partial
-    # sums, and the causal size serves it too.
-    need_nc = lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 0)
+    # One key block: a non-causal launch splits its two query tiles too.
+    assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 0) == need
     assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 1) == need
-    assert need_nc == need - 2 * a256(4 * 2 * 256 * 64)
-    assert bwd_qk(ws_bytes=need_nc - 1, causal=0) == _lib.FA_ERR_INVALID_ARG
+    # 192 key blocks (B2 H12 N2048 D64): a non-causal launch runs one query
+    # segment, so its workspace has no partial sums; a causal one runs three.
+    # The causal size serves either mask.
+    nc = lib.fa_bwd_qk_workspace_bytes_for(2, 12, 2048, 2048, 64, 0)
+    c = lib.fa_bwd_qk_workspace_bytes_for(2, 12, 2048, 2048, 64, 1)
+    assert c == lib.fa_bwd_workspace_bytes(2, 12, 2048, 64)
+    assert c - nc == 2 * a256(4 * 3 * 24 * 2048 * 64)
+    assert bwd_qk(ws_bytes=nc - 1, causal=0, B=2, H=12, Nq=2048, Nk=2048) == _lib.FA_ERR_INVALID_ARG
     assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 128, 256, 64, 2) == 0
     assert lib.fa_bwd_qk_workspace_bytes_for(1, 1, 0, 256, 64, 0) == 0
     assert bwd_qk(Nk=0) == _lib.FA_ERR_INVALID_ARG

@@ -105,7 +105,8 @@ def _check_rows(inp, causal, what, nrows=48):
 @pytest.mark.parametrize("N", [1, 17, 129, 300])
 def test_poisoned_small(poisoned, N, D, causal):
     """4-wave forwards, the head_dim-128 split form (non-causal), the
-    backward with query segments (causal) and without, ragged tails."""
+    backward with query segments (causal, and non-causal past one query
+    tile) and without, ragged tails."""
     what = f"poisoned N={N} D={D} causal={causal}"
     _say("case", what)
     _check_full(random_qkv(2, N, 3, D, "bf16", seed=9100 + N + D), causal, what)
@@ -173,7 +174,8 @@ def test_poisoned_fp8(poisoned, D, causal, N):
 
 TILE_CONFIGS = [
     # (label, B, H, N, D, causal): the launch form each one selects
-    ("d64 4-wave fwd, unsegmented bwd", 2, 4, 1000, 64, False),
+    ("d64 4-wave fwd, unsegmented bwd", 4, 12, 1024, 64, False),
+    ("d64 segmented non-causal bwd", 2, 4, 1000, 64, False),
     ("d64 8-wave fwd", 4, 16, 2048, 64, True),
     ("d64 segmented bwd", 1, 2, 3000, 64, True),
     ("d128 paired fwd, segmented bwd", 1, 4, 2048, 128, True),
