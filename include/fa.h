@@ -147,8 +147,8 @@ size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits)
 
 /* A split count for fa_fwd_split: 1 unless the unsplit launch has at most
  * one wave (32 query rows) per SIMD of the device and the keys allow splits
- * of at least 2048; then enough splits for about four waves per SIMD, at
- * most 64. */
+ * of at least 2048 (1024 when Nq <= 64); then enough splits for about four
+ * waves per SIMD, at most 64. */
 int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
 
 /*

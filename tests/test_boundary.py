@@ -323,16 +323,21 @@ def test_split_entry_points_without_launch():
 
     # Split counts: launches with more than one wave per SIMD are not split
     # (the four sweep workloads; head_dim-128 key-group forms count twice);
-    # narrow launches get splits of at least 2048 keys.
+    # narrow launches get splits of at least 2048 (or 1024) keys.
     assert lib.fa_fwd_split_count(1, 16, 16384, 16384, 64, 1) == 1
     assert lib.fa_fwd_split_count(1, 8, 8192, 8192, 128, 1) == 1
     assert lib.fa_fwd_split_count(2, 12, 2048, 2048, 64, 0) == 1
     assert lib.fa_fwd_split_count(2, 12, 512, 512, 64, 0) == 1
     assert lib.fa_fwd_split_count(1, 8, 4096, 4096, 128, 1) == 1
     assert lib.fa_fwd_split_count(1, 2, 16384, 16384, 64, 1) == 4
-    assert lib.fa_fwd_split_count(1, 16, 1, 16384, 64, 1) == 8
-    assert lib.fa_fwd_split_count(8, 8, 1, 8192, 128, 1) == 4
-    assert lib.fa_fwd_split_count(1, 16, 1, 2048, 64, 1) == 1
+    # Blocks of at most 64 query rows split down to 1024 keys, longer ones
+    # to 2048.
+    assert lib.fa_fwd_split_count(1, 16, 1, 16384, 64, 1) == 16
+    assert lib.fa_fwd_split_count(1, 16, 64, 16384, 64, 1) == 16
+    assert lib.fa_fwd_split_count(1, 16, 65, 16384, 64, 1) == 8
+    assert lib.fa_fwd_split_count(8, 8, 1, 8192, 128, 1) == 8
+    assert lib.fa_fwd_split_count(1, 16, 1, 2048, 64, 1) == 2
+    assert lib.fa_fwd_split_count(1, 16, 1, 1023, 64, 1) == 1
     assert lib.fa_fwd_split_count(1, 1, 1, 500, 64, 0) == 1
     assert lib.fa_fwd_split_count(0, 1, 1, 500, 64, 0) == 1
 
