@@ -492,16 +492,22 @@ static hipError_t launch_fwd64_nw(const FwdParams& p_in, bool masked, hipStream_
   return hipGetLastError();
 }
 
-// 8 waves (256 query rows) per workgroup when that still gives at least two
-// workgroups per compute unit, else 4 waves (128 rows).  Non-causal launches
-// run the causal kernel with the mask offset at Nk: every key is visible and
-// only the key tail is masked.
+// 8 waves (256 query rows) per workgroup when that gives at least two
+// workgroups per compute unit (non-causal) or four (causal), else 4 waves
+// (128 rows).  Causal work per block varies, and the finer 4-wave blocks
+// (three resident per compute unit) balance it better up to about 900
+// 256-row blocks.  Measured forward ms, 8 against 4 waves: causal B1 H10
+// N16384 (640 blocks) 0.439 / 0.400, B6 H8 N4096 (768) 0.144 / 0.134, B4
+// H8 N4096 (512) 0.097 / 0.092, B1 H14 N16384 (896) 0.559 / 0.556, B1 H16
+// N16384 (1024) 0.601 / 0.621; non-causal B2 H8 N8192 (512) 0.293 / 0.315.
+// Non-causal launches run the causal kernel with the mask offset at Nk:
+// every key is visible and only the key tail is masked.
 template <typename T>
 hipError_t launch_fwd64_t(const FwdParams& p_in, bool causal, hipStream_t s) {
   FwdParams p = p_in;
   if (!causal) p.off = p.Nk;
   const int64_t wg8 = static_cast<int64_t>(p.B) * p.H * ((p.N + 255) / 256);
-  if (wg8 >= 512) return launch_fwd64_nw<T, 8, true>(p, causal, s);
+  if (wg8 >= (causal ? 1024 : 512)) return launch_fwd64_nw<T, 8, true>(p, causal, s);
   return launch_fwd64_nw<T, 4, true>(p, causal, s);
 }
 

@@ -120,11 +120,18 @@ def test_poisoned_key_splits(poisoned, D, causal, splits):
 
 
 def test_poisoned_eight_wave_forward(poisoned):
-    """B*H*ceil(N/256) = 512: the 8-wave head_dim-64 forward (interleaved
-    pipeline steps) and the unsegmented backward."""
-    what = "poisoned B=4 H=16 N=2048 D=64 causal"
+    """B*H*ceil(N/256) = 1024: the causal 8-wave head_dim-64 forward
+    (interleaved pipeline steps) and the unsegmented backward."""
+    what = "poisoned B=8 H=16 N=2048 D=64 causal"
     _say("case", what)
-    _check_rows(random_qkv(4, 2048, 16, 64, "bf16", seed=9300), True, what, nrows=16)
+    _check_rows(random_qkv(8, 2048, 16, 64, "bf16", seed=9300), True, what, nrows=16)
+
+
+def test_poisoned_eight_wave_forward_non_causal(poisoned):
+    """B*H*ceil(N/256) = 512, non-causal: the 8-wave head_dim-64 forward."""
+    what = "poisoned B=4 H=16 N=2048 D=64 non-causal"
+    _say("case", what)
+    _check_rows(random_qkv(4, 2048, 16, 64, "bf16", seed=9310), False, what, nrows=16)
 
 
 @pytest.mark.parametrize("N", [1100, 1500])
@@ -176,7 +183,7 @@ TILE_CONFIGS = [
     # (label, B, H, N, D, causal): the launch form each one selects
     ("d64 4-wave fwd, unsegmented bwd", 4, 12, 1024, 64, False),
     ("d64 segmented non-causal bwd", 2, 4, 1000, 64, False),
-    ("d64 8-wave fwd", 4, 16, 2048, 64, True),
+    ("d64 8-wave fwd", 8, 16, 2048, 64, True),
     ("d64 segmented bwd", 1, 2, 3000, 64, True),
     ("d128 paired fwd, segmented bwd", 1, 4, 2048, 128, True),
     ("d128 4-wave fwd", 2, 4, 900, 128, True),
