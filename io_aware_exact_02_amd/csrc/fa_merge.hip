@@ -81,25 +81,55 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeParams p) {
   const int bh = static_cast<int>(row / p.N);
   const int b = bh / p.H, h = bh % p.H;
 
+  // The loads of several splits are issued before any of them is used, so
+  // that a row's latency is a few memory round trips rather than one per
+  // split (decoding-like launches have few rows and many splits).  The sums
+  // still run in split order.
   float m = -INFINITY;
-  for (int s = 0; s < p.S; ++s) m = fmaxf(m, p.lse_part[s * rows + row]);
+  {
+    int s = 0;
+    for (; s + 8 <= p.S; s += 8) {
+      float ls[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ls[e] = p.lse_part[(s + e) * rows + row];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, ls[e]);
+    }
+    for (; s < p.S; ++s) m = fmaxf(m, p.lse_part[s * rows + row]);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (m > -INFINITY) {
     float tot = 0.0f;
-    for (int s = 0; s < p.S; ++s) {
-      const float ls = p.lse_part[s * rows + row];
-      if (ls == -INFINITY) continue;
+    // One split's contribution; an empty split (no key seen) has weight 0.
+    auto add = [&](float ls, const f32x4& a0, const f32x4& a1) {
+      if (ls == -INFINITY) return;
       const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
       tot += w;
-      const float* op = p.o_part + (s * rows + row) * D + part * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(op);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(op + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[e] += w * a0[e];
         acc[e + 4] += w * a1[e];
       }
+    };
+    int s = 0;
+    for (; s + 4 <= p.S; s += 4) {
+      float ls[4];
+      f32x4 a0[4], a1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ls[e] = p.lse_part[(s + e) * rows + row];
+        const float* op = p.o_part + ((s + e) * rows + row) * D + part * 8;
+        a0[e] = *reinterpret_cast<const f32x4*>(op);
+        a1[e] = *reinterpret_cast<const f32x4*>(op + 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) add(ls[e], a0[e], a1[e]);
+    }
+    for (; s < p.S; ++s) {
+      const float* op = p.o_part + (s * rows + row) * D + part * 8;
+      add(p.lse_part[s * rows + row], *reinterpret_cast<const f32x4*>(op),
+          *reinterpret_cast<const f32x4*>(op + 4));
     }
     const float inv = 1.0f / tot;
 #pragma unroll
