@@ -65,9 +65,11 @@ static hipError_t launch_merge_t(const MergeParams& p, hipStream_t s) {
 }
 
 // The partial results of a key-split forward, fp32 and normalised per split:
-// the same rule over the splits, rounded to the output type once.  One row
-// (b, h, n) per D/8 threads, 8 elements each; splits that saw no key of the
-// row (LSE -inf) carry no weight.
+// the same rule over the splits, rounded to the output type once; splits
+// that saw no key of the row (LSE -inf) carry no weight.  One row (b, h, n)
+// per D/8 threads, 8 elements each.  The loads of several splits are issued
+// before any of them is used, so that a row's latency is a few memory round
+// trips rather than one per split; the sums still run in split order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeParams p) {
   constexpr int TPR = D / 8;
@@ -81,10 +83,6 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeParams p) {
   const int bh = static_cast<int>(row / p.N);
   const int b = bh / p.H, h = bh % p.H;
 
-  // The loads of several splits are issued before any of them is used, so
-  // that a row's latency is a few memory round trips rather than one per
-  // split (decoding-like launches have few rows and many splits).  The sums
-  // still run in split order.
   float m = -INFINITY;
   {
     int s = 0;
@@ -141,12 +139,86 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeParams p) {
   if (part == 0) p.lse[row] = lse;
 }
 
+// The same merge for launches with few rows (decoding-like: few rows, many
+// splits): one wave per row (b, h, n), lane (g, part) taking the 8 elements
+// part*8.. of every G-th split from g, the G groups' maxima and sums then
+// combined across the wave in a fixed order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void split_merge_wave_kernel(SplitMergeParams p) {
+  constexpr int TPR = D / 8;  // lanes per split of a row
+  constexpr int G = 64 / TPR;  // split groups per row
+  constexpr int RPB = 256 / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int part = lane % TPR;
+  const int g = lane / TPR;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
+  // Wave-uniform: every lane of a wave serves the same row.
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + (tid >> 6);  // (b*H + h)*N + n
+  if (row >= rows) return;
+  const int n = static_cast<int>(row % p.N);
+  const int bh = static_cast<int>(row / p.N);
+  const int b = bh / p.H, h = bh % p.H;
+
+  float m = -INFINITY;
+  for (int s = g; s < p.S; s += G) m = fmaxf(m, p.lse_part[s * rows + row]);
+#pragma unroll
+  for (int o = TPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float tot = 0.0f;
+  if (m > -INFINITY) {  // the same for every lane of the row
+    for (int s = g; s < p.S; s += G) {
+      const float ls = p.lse_part[s * rows + row];
+      const float* op = p.o_part + (s * rows + row) * D + part * 8;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(op);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(op + 4);
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+      tot += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * a0[e];
+        acc[e + 4] += w * a1[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int o = TPR; o < 64; o <<= 1) {
+    tot += __shfl_xor(tot, o, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+  float lse = -INFINITY;
+  if (m > -INFINITY) {
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    lse = m + __builtin_logf(tot);
+  }
+  if (g == 0) {
+    stg16(p.o + b * p.so.b + static_cast<int64_t>(n) * p.so.n + h * p.so.h + part * 8,
+          pack8<T>(acc));
+    if (part == 0) p.lse[row] = lse;
+  }
+}
+
 template <typename T, int D>
 static hipError_t launch_split_merge_t(const SplitMergeParams& p, hipStream_t s) {
-  constexpr int RPB = 256 / (D / 8);
   const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.N;
-  const unsigned blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL((split_merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s, p);
+  // Few rows (at most 4096, e.g. one query row per head): a wave per row, so
+  // that the splits are read in parallel.  Many rows: D/8 threads per row,
+  // which already keeps enough loads in flight.  Measured (key-split forward
+  // with its merge, B1 H16 N_q=1 N_k=16384, 16 splits): 22.5 -> 20.6 us;
+  // with 8192 rows (N_q=512) the thread form was 3% faster.
+  if (rows <= 4096) {
+    constexpr int RPB = 256 / 64;
+    const unsigned blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
+    hipLaunchKernelGGL((split_merge_wave_kernel<T, D>), dim3(blocks), dim3(256), 0, s, p);
+  } else {
+    constexpr int RPB = 256 / (D / 8);
+    const unsigned blocks = static_cast<unsigned>((rows + RPB - 1) / RPB);
+    hipLaunchKernelGGL((split_merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
