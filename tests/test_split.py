@@ -77,11 +77,13 @@ def _check_against_unsplit(o, lse, o1, lse1, vmax, dtype, what):
     assert np.all(np.abs(o - o1) <= bound), f"{what}: O vs unsplit {np.max(np.abs(o - o1)):.3e}"
 
 
-# (B, H, Nq, Nk, D, causal, dtype, num_splits).  Together they reach every
-# forward kernel form (head_dim 64 with 4 and 8 waves, the split key-group
-# form of head_dim 128 causal-paired and non-causal, the plain head_dim-128
-# causal form), ranges a row cannot see, rows that see no key, a split count
-# above the number of 128-key ranges, and ragged key tails.
+# (B, H, Nq, Nk, D, causal, dtype, num_splits).  Together they reach the
+# forward kernel forms a split launch of this size takes (head_dim 64 with 4
+# waves, the split key-group form of head_dim 128 causal-paired and
+# non-causal, the plain head_dim-128 causal form), both forms of the merge
+# (one wave per row up to 4096 rows, D/8 threads per row above), ranges a
+# row cannot see, rows that see no key, a split count above the number of
+# 128-key ranges, and ragged key tails.
 CASES = [
     (1, 4, 1, 1000, 64, True, "bf16", 4),      # one new query against a history
     (1, 4, 1, 1000, 128, False, "f16", 7),
@@ -95,6 +97,7 @@ CASES = [
     (1, 2, 257, 4096, 64, False, "bf16", 64),  # many splits
     (1, 2, 64, 129, 64, False, "f16", 256),    # more splits than 128-key ranges
     (2, 2, 1000, 3000, 128, False, "bf16", 3),
+    (2, 4, 600, 1800, 64, True, "bf16", 3),    # 4800 rows: the per-thread merge
 ]
 
 
