@@ -63,6 +63,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2516.6  # MI355X dense bf16/fp16: 256 CU x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_TBPS = 8.0  # MI355X HBM3E, published
 METRIC = "attention fwd+bwd TFLOPs/s and % of MFMA bf16 peak, N=512..16K, 1 GPU"
 SWEEP = ("c2", "c3", "c4", "c5")
 DOMINANT = "c5"
@@ -344,19 +345,25 @@ def head_shard(torch, fa):
 
 def split_kv(torch, fa):
     """Forward of short query blocks against a long key history (one new row
-    per head, or a 512-row chunk of a long context), causal mask aligned to
-    the last key: the whole key range per workgroup (num_splits=1) against
-    the key-split forward at fa_fwd_split_count's choice (partial results
-    combined exactly by a second kernel).  10 timed launches after 3
-    warm-ups each.  ``kv_gb_per_s`` is the K and V bytes of one call over
-    the split time: these launches stream K and V once."""
+    per head, a batch of them, or a 512-row chunk of a long context), causal
+    mask aligned to the last key: the whole key range per workgroup
+    (num_splits=1) against the key-split forward at fa_fwd_split_count's
+    choice (partial results combined exactly by a second kernel).  One or two
+    rows per head run the vector-unit kernel, more the tiled ones.  Each call
+    goes straight to fa_fwd_split with a workspace allocated beforehand, so
+    that the host's per-call work stays below the GPU time; 20 timed calls
+    after 3 warm-ups each.  ``kv_gb_per_s`` is the K and V bytes of one call
+    over the split time (these launches stream K and V once) and
+    ``hbm_frac`` that rate over the 8 TB/s peak."""
+    import ctypes
     from io_aware_exact_02_amd import _lib
     from workloads import random_qkv
     lib = _lib.load()
     dev = torch.device("cuda")
-    shapes = [(1, 16, 1, 16384, 64), (1, 16, 512, 16384, 64), (8, 8, 1, 8192, 128)]
+    shapes = [(1, 16, 1, 16384, 64), (8, 8, 1, 8192, 128), (64, 32, 1, 2048, 128),
+              (1, 16, 512, 16384, 64)]
 
-    def timed(fn, iters=10, warm=3):
+    def timed(fn, iters=20, warm=3):
         for _ in range(warm):
             fn()
         stream = torch.cuda.current_stream(dev)
@@ -377,14 +384,29 @@ def split_kv(torch, fa):
         o = torch.empty_like(q)
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
         S = int(lib.fa_fwd_split_count(B, H, Nq, Nk, D, 1))
-        t1 = timed(lambda: fa.fwd(q, k, v, causal=True, out=o, lse=lse, num_splits=1))
-        ts = timed(lambda: fa.fwd(q, k, v, causal=True, out=o, lse=lse, num_splits=S))
+        nbytes = int(lib.fa_fwd_split_workspace_bytes(B, H, Nq, D, S))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        st = _lib.FwdStrides(*(_lib.Stride3(*t.stride()[:3]) for t in (q, k, v, o)))
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+        def call(splits):
+            status = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), B, H, Nq, Nk, D, 1, D ** -0.5,
+                                      _lib.FA_BF16, ctypes.byref(st), splits, ws.data_ptr(),
+                                      nbytes, stream)
+            if status != _lib.FA_OK:
+                raise RuntimeError(f"fa_fwd_split: status {status}")
+
+        t1 = timed(lambda: call(1))
+        ts = timed(lambda: call(S))
         kv_bytes = 2 * B * H * Nk * D * 2
+        gbs = kv_bytes / ts / 1e6
         rows.append({"shape": f"B={B} H={H} Nq={Nq} Nk={Nk} D={D} bf16 causal",
+                     "kernel": "vector-unit" if Nq <= 2 else "tiled",
                      "num_splits": S, "unsplit_ms": round(t1, 4), "split_ms": round(ts, 4),
-                     "speedup": round(t1 / ts, 2),
-                     "kv_gb_per_s": round(kv_bytes / ts / 1e6, 1)})
-        del q, k, v, o, lse
+                     "speedup": round(t1 / ts, 2), "kv_gb_per_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / (HBM_PEAK_TBPS * 1e3), 3)})
+        del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
     return rows
 
@@ -525,6 +547,21 @@ def gfx_clock_sampler():
     return start, finish
 
 
+def copy_calibration(torch, dev, mib):
+    """One plain elementwise kernel that reads and writes `mib` MiB: what
+    rocprofv3's FETCH_SIZE and WRITE_SIZE read for it scales theirs for the
+    attention kernels."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)  # one read + one write of n*4 bytes
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -553,6 +590,9 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run one plain elementwise kernel that reads and "
                          "writes this many MiB (calibrates HBM byte counters)")
+    ap.add_argument("--only-split-kv", action="store_true",
+                    help="run only the short-query / long-history forward measurement "
+                         "(and the counter calibration) and print its rows as one JSON line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -569,6 +609,11 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
+    if args.only_split_kv:
+        rows = split_kv(torch, fa)
+        copy_calibration(torch, dev, args.copy_calibration_mib)
+        print(json.dumps({"split_kv": rows, "data": "synthetic"}), flush=True)
+        return 0
     names = [n.strip() for n in args.workloads.split(",") if n.strip()]
     cases = []
     for name in names:
@@ -719,14 +764,7 @@ def main(argv=None):
                    "achieved_g_adds_per_s": round(adds / dkdv_ms / 1e6, 1),
                    "achieved_payload_tb_per_s": round(4 * adds / dkdv_ms / 1e9, 3)}
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)  # one read + one write of n*4 bytes
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(torch, dev, args.copy_calibration_mib)
 
     memory = None
     if not args.no_memory and "c3" in names:

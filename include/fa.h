@@ -92,6 +92,11 @@ typedef struct {
  *             (1/sqrt(D) is the formula's choice).
  *   strides : NULL or the element strides of q, k, v, o.
  * o must not alias q, k or v.  Extra device memory: none.
+ * Launches with at most two query rows per (batch, head) run a vector-unit
+ * kernel that streams K and V through registers and keeps the softmax
+ * weights in fp32; larger ones run the tiled matrix-core kernels, which
+ * round the weights to dtype for the P.V product.  Both meet the same
+ * bound against the exact result.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int D, int causal, float scale, int dtype,
@@ -145,10 +150,13 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
  * Returns 0 for invalid sizes. */
 size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits);
 
-/* A split count for fa_fwd_split: 1 unless the unsplit launch has at most
- * one wave (32 query rows) per SIMD of the device and the keys allow splits
- * of at least 2048 (1024 when Nq <= 64); then enough splits for about four
- * waves per SIMD, at most 64. */
+/* A split count for fa_fwd_split.  Nq <= 2 (the vector-unit kernel, one
+ * 4-wave workgroup per (batch, head, split)): 1 when B*H >= 256, else
+ * ceil(256 / (B*H)) limited to floor(Nk / 1024) and 64.  Larger Nq: 1
+ * unless the unsplit launch has at most one wave (32 query rows) per SIMD
+ * of the device and the keys allow splits of at least 2048 (1024 when
+ * Nq <= 64); then enough splits for about four waves per SIMD, at most 64.
+ * The result is at least 1. */
 int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
 
 /*

@@ -26,7 +26,8 @@ LIB = os.path.join(PKG, "libfa.so")
 POISON_LIB = os.path.join(PKG, "libfa_poison.so")
 PROBE = os.path.join(PKG, "atomic_probe")
 
-SOURCES = ["fa_fwd.hip", "fa_fwd64.hip", "fa_fwd8.hip", "fa_bwd.hip", "fa_merge.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd64.hip", "fa_fwd8.hip", "fa_decode.hip", "fa_bwd.hip", "fa_merge.hip",
+           "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled: hipcc would otherwise fuse scalar

@@ -138,6 +138,15 @@ int make_fwd_params(fa::FwdParams& p, const void* q, const void* k, const void* 
 
 constexpr int kMaxSplits = 256;
 
+// The 16-bit forward for a parameter block: at most two query rows per head
+// go to the vector-unit kernel that streams K and V through registers
+// (fa_decode.hip), more to the tiled matrix-core kernels.
+hipError_t launch_forward(const fa::FwdParams& p, int dtype, int D, int causal,
+                          hipStream_t stream) {
+  if (p.N <= fa::kDecodeMaxRows) return fa::launch_decode(p, dtype, D, causal, stream);
+  return fa::launch_fwd(p, dtype, D, causal, stream);
+}
+
 // Keys per split for a requested split count: ceil(Nk / S) rounded up to a
 // multiple of 128 (the widest K/V tile), so that every split starts on a
 // tile boundary.
@@ -265,7 +274,7 @@ int fa_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, 
   const int st = make_fwd_params(p, q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale, dtype,
                                  strides);
   if (st != FA_OK) return st;
-  const hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+  const hipError_t e = launch_forward(p, dtype, D, causal, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -277,6 +286,21 @@ size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits)
 
 int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal) {
   if (rows_of(B, H, Nq) < 0 || Nk <= 0) return 1;
+  if (Nq <= fa::kDecodeMaxRows) {
+    // The vector-unit kernel, one 4-wave workgroup per (head, split): aim for
+    // 256 workgroups, each with at least 1024 keys.  Measured on MI355X
+    // (forward with merge, us, bf16; S = splits): B1 H16 N_k=16384 D64
+    // causal: S8 16.9, S16 15.8, S32 16.1; B1 H32 N_q=2 N_k=8192 D128
+    // causal: S4 34.6, S8 27.1, S16 27.3; B4 H16 N_k=8192 D64: S4 25.7, S16
+    // 25.4; B1 H16 N_k=4096 D64: S4 10.1; B32 H16 N_k=4096 D64: S1 100.6,
+    // S4 103.8.
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    if (bh >= 256) return 1;
+    int64_t s = (256 + bh - 1) / bh;
+    s = s < Nk / 1024 ? s : Nk / 1024;
+    s = s < 64 ? s : 64;
+    return s > 1 ? static_cast<int>(s) : 1;
+  }
   // Waves of the unsplit launch: one per 32 query rows, two where head_dim
   // 128 runs the two-key-group form (non-causal, or causal from 1024 rows
   // when 256-row blocks leave CUs free; see launch_fwd).
@@ -319,7 +343,7 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
       return FA_ERR_UNSUPPORTED;
   }
   if (S == 1) {
-    const hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+    const hipError_t e = launch_forward(p, dtype, D, causal, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
   const SplitWorkspace w = split_workspace(B, H, Nq, D, num_splits);
@@ -328,7 +352,7 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
   p.split_len = static_cast<int>(len);
   p.o_part = reinterpret_cast<float*>(ws);
   p.lse_part = reinterpret_cast<float*>(ws + w.lse);
-  hipError_t e = fa::launch_fwd(p, dtype, D, causal, stream);
+  hipError_t e = launch_forward(p, dtype, D, causal, stream);
   if (e != hipSuccess) return FA_ERR_HIP;
   fa::SplitMergeParams m{};
   m.o_part = p.o_part;

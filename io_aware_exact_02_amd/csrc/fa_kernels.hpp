@@ -112,5 +112,10 @@ int bwd_segments(int B, int H, int Nq, int Nk, int D, bool causal);
 hipError_t launch_merge(const MergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_split_merge(const SplitMergeParams& p, int dtype, int D, hipStream_t s);
 hipError_t launch_fwd8(const Fwd8Params& p, int out_dtype, int D, int causal, hipStream_t s);
+// The vector-unit forward for at most kDecodeMaxRows query rows per (batch,
+// head) (fa_decode.hip): with o_part set, the split partials of FwdParams;
+// otherwise (one split) o and lse.
+constexpr int kDecodeMaxRows = 2;
+hipError_t launch_decode(const FwdParams& p, int dtype, int D, int causal, hipStream_t s);
 
 }  // namespace fa

@@ -141,12 +141,16 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeParams p) {
 
 // The same merge for launches with few rows (decoding-like: few rows, many
 // splits): one wave per row (b, h, n), lane (g, part) taking the 8 elements
-// part*8.. of every G-th split from g, the G groups' maxima and sums then
-// combined across the wave in a fixed order.
+// part*8.. of every G-th split from g.  A lane issues the loads of U of its
+// splits at once and keeps a running maximum (its sum and outputs scaled by
+// 2^(m_old - m_new) when it grows), so that up to U*G splits cost one memory
+// round trip; the G groups are then combined across the wave in a fixed
+// order, each scaled to the row's maximum.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void split_merge_wave_kernel(SplitMergeParams p) {
   constexpr int TPR = D / 8;  // lanes per split of a row
   constexpr int G = 64 / TPR;  // split groups per row
+  constexpr int U = 4;         // splits a lane loads at once
   constexpr int RPB = 256 / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -160,40 +164,65 @@ __global__ __launch_bounds__(256) void split_merge_wave_kernel(SplitMergeParams 
   const int bh = static_cast<int>(row / p.N);
   const int b = bh / p.H, h = bh % p.H;
 
-  float m = -INFINITY;
-  for (int s = g; s < p.S; s += G) m = fmaxf(m, p.lse_part[s * rows + row]);
-#pragma unroll
-  for (int o = TPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // natural-log units, as the partial LSEs
   float tot = 0.0f;
-  if (m > -INFINITY) {  // the same for every lane of the row
-    for (int s = g; s < p.S; s += G) {
-      const float ls = p.lse_part[s * rows + row];
-      const float* op = p.o_part + (s * rows + row) * D + part * 8;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(op);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(op + 4);
-      if (ls == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = g; s0 < p.S; s0 += U * G) {
+    float ls[U];
+    f32x4 a0[U], a1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * G;
+      if (s < p.S) {
+        ls[u] = p.lse_part[s * rows + row];
+        const float* op = p.o_part + (s * rows + row) * D + part * 8;
+        a0[u] = *reinterpret_cast<const f32x4*>(op);
+        a1[u] = *reinterpret_cast<const f32x4*>(op + 4);
+      } else {
+        ls[u] = -INFINITY;  // no such split: no weight
+        a0[u] = a1[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, ls[u]);
+    if (mn == -INFINITY) continue;  // no key seen by these splits or before
+    const float alpha = __builtin_amdgcn_exp2f((m - mn) * kLog2e);  // 0 while m = -inf
+    tot *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ls[u] == -INFINITY) continue;  // a split that saw no key of the row
+      const float w = __builtin_amdgcn_exp2f((ls[u] - mn) * kLog2e);
       tot += w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[e] += w * a0[e];
-        acc[e + 4] += w * a1[e];
+        acc[e] += w * a0[u][e];
+        acc[e + 4] += w * a1[u][e];
       }
     }
+    m = mn;
   }
+  float M = m;
 #pragma unroll
-  for (int o = TPR; o < 64; o <<= 1) {
-    tot += __shfl_xor(tot, o, 64);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
-  }
+  for (int o = TPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   float lse = -INFINITY;
-  if (m > -INFINITY) {
+  if (M > -INFINITY) {  // the same for every lane of the row
+    const float f = __builtin_amdgcn_exp2f((m - M) * kLog2e);  // 0 for a group with m = -inf
+    tot *= f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= f;
+#pragma unroll
+    for (int o = TPR; o < 64; o <<= 1) {
+      tot += __shfl_xor(tot, o, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    }
     const float inv = 1.0f / tot;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= inv;
-    lse = m + __builtin_logf(tot);
+    lse = M + __builtin_logf(tot);
   }
   if (g == 0) {
     stg16(p.o + b * p.so.b + static_cast<int64_t>(n) * p.so.n + h * p.so.h + part * 8,

@@ -4,6 +4,9 @@ attention kernels, measured on ``bench.py``.
     python -m io_aware_exact_02_amd.rocprof_harness --raw /tmp/prof \\
         [--workloads c2,c3,c4,c5] [--summary-dir profiles]
 
+(``--workloads split_kv`` profiles bench.py's short-query / long-history
+forwards instead: ``bench.py --only-split-kv``.)
+
 Four rocprofv3 runs of ``bench.py`` (each its own process; counters never
 share a run with tracing):
 
@@ -68,7 +71,7 @@ def grid_size(r) -> str:
 
 
 def short_name(kernel: str) -> str:
-    k = kernel.replace("void ", "").replace("fa::", "")
+    k = kernel.replace("void ", "").replace("(anonymous namespace)::", "").replace("fa::", "")
     return k.split("(")[0].strip()
 
 
@@ -83,6 +86,10 @@ def run(cmd, timeout, log):
 
 
 def bench_cmd(workloads, steps, warmup, calib_mib):
+    if workloads == "split_kv":
+        # The short-query / long-history forwards alone (bench.py split_kv).
+        return [sys.executable, BENCH, "--only-split-kv", "--copy-calibration-mib",
+                str(calib_mib)]
     return [sys.executable, BENCH, "--steps", str(steps), "--warmup", str(warmup), "--cpu-seconds", "0",
             "--no-memory", "--no-pages-sweep", "--no-mha", "--no-shard", "--no-split",
             # No kernels after the timed region: the summary's "timed" column

@@ -332,10 +332,18 @@ def test_split_entry_points_without_launch():
     assert lib.fa_fwd_split_count(1, 2, 16384, 16384, 64, 1) == 4
     # Blocks of at most 64 query rows split down to 1024 keys, longer ones
     # to 2048.
-    assert lib.fa_fwd_split_count(1, 16, 1, 16384, 64, 1) == 16
     assert lib.fa_fwd_split_count(1, 16, 64, 16384, 64, 1) == 16
     assert lib.fa_fwd_split_count(1, 16, 65, 16384, 64, 1) == 8
-    assert lib.fa_fwd_split_count(8, 8, 1, 8192, 128, 1) == 8
+    assert lib.fa_fwd_split_count(1, 16, 3, 16384, 64, 1) == 16
+    # One or two rows (the vector-unit kernel): 256 workgroups of at least
+    # 1024 keys, none once B*H reaches 256.
+    assert lib.fa_fwd_split_count(1, 16, 1, 16384, 64, 1) == 16
+    assert lib.fa_fwd_split_count(1, 8, 2, 32768, 128, 0) == 32
+    assert lib.fa_fwd_split_count(1, 32, 2, 8192, 128, 1) == 8
+    assert lib.fa_fwd_split_count(8, 8, 1, 8192, 128, 1) == 4
+    assert lib.fa_fwd_split_count(1, 8, 1, 3000, 128, 1) == 2
+    assert lib.fa_fwd_split_count(16, 16, 1, 65536, 64, 1) == 1
+    assert lib.fa_fwd_split_count(1, 1, 2, 1 << 20, 64, 0) == 64
     assert lib.fa_fwd_split_count(1, 16, 1, 2048, 64, 1) == 2
     assert lib.fa_fwd_split_count(1, 16, 1, 1023, 64, 1) == 1
     assert lib.fa_fwd_split_count(1, 1, 1, 500, 64, 0) == 1

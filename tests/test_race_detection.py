@@ -8,7 +8,8 @@ Two checks:
   barrier, a tile that is not loaded, a buffer reused too early) then
   returns NaN instead of stale data.  The cases below run every launch form
   -- 4- and 8-wave head_dim-64 forwards, the head_dim-128 plain and split
-  forms, key splits, the FP8 forward, the backward with and without query
+  forms, key splits, the vector-unit forward of one or two rows, the FP8
+  forward, the backward with and without query
   segments, ragged tails and head counts off the XCD grid -- through the
   poisoned build and check them against the oracle.
 * Determinism: three runs of each tile configuration give bitwise equal O,
@@ -110,6 +111,25 @@ def test_poisoned_small(poisoned, N, D, causal):
     what = f"poisoned N={N} D={D} causal={causal}"
     _say("case", what)
     _check_full(random_qkv(2, N, 3, D, "bf16", seed=9100 + N + D), causal, what)
+
+
+@pytest.mark.parametrize("Nq,Nk,D,causal,splits", [(1, 3000, 64, True, 5), (2, 1500, 128, False, 3),
+                                                 (2, 2, 64, True, 1)])
+def test_poisoned_decode(poisoned, Nq, Nk, D, causal, splits):
+    """The vector-unit forward of one or two rows (its LDS combine of the
+    four waves), split and unsplit, and the backward after it."""
+    what = f"poisoned decode Nq={Nq} Nk={Nk} D={D} causal={causal} splits={splits}"
+    _say("case", what)
+    a = random_qkv(1, Nq, 3, D, "bf16", seed=9250 + Nk + D)
+    b = random_qkv(1, Nk, 3, D, "bf16", seed=9251 + Nk + D)
+    inp = {"q": a["q"], "do": a["do"], "k": b["k"], "v": b["v"]}
+    got = _run(inp, causal, splits)
+    O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=causal)
+    assert np.max(np.abs(got["O"] - O)) <= O_TOL, f"{what}: O"
+    assert np.max(np.abs(got["LSE"] - LSE)) <= LSE_TOL, f"{what}: LSE"
+    refs = oa.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], causal=causal)
+    for name, ref in zip(("dQ", "dK", "dV"), refs):
+        _grad_ok(name, got[name], ref, what)
 
 
 @pytest.mark.parametrize("D,causal,splits", [(64, True, 3), (128, False, 2), (64, False, 5)])
