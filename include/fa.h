@@ -152,11 +152,12 @@ size_t fa_fwd_split_workspace_bytes(int B, int H, int Nq, int D, int num_splits)
 
 /* A split count for fa_fwd_split.  Nq <= 2 (the vector-unit kernel, one
  * 4-wave workgroup per (batch, head, split)): 1 when B*H >= 256, else
- * ceil(256 / (B*H)) limited to floor(Nk / 1024) and 64.  Larger Nq: 1
- * unless the unsplit launch has at most one wave (32 query rows) per SIMD
- * of the device and the keys allow splits of at least 2048 (1024 when
- * Nq <= 64); then enough splits for about four waves per SIMD, at most 64.
- * The result is at least 1. */
+ * ceil(256 / (B*H)) limited to floor(Nk / 1024) and 64.  Larger Nq, with W
+ * the waves of the unsplit launch (one per 32 query rows; two at head_dim
+ * 128 in its two-key-group forms): 1 when W > 1024 (one wave per SIMD of
+ * the device); else S = min(ceil(4096 / W), 64, floor(Nk / 2048)), and
+ * where W*S < 1024 instead min(ceil(4096 / W), 64, floor(Nk / 1024),
+ * ceil(1024 / W)).  The result is at least 1. */
 int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
 
 /*

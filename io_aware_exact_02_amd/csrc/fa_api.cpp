@@ -308,19 +308,27 @@ int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal) {
   const int64_t wg256 = static_cast<int64_t>(B) * H * ((Nq + 255) / 256);
   if (D == 128 && (!causal || (Nq >= 1024 && wg256 <= 256))) waves *= 2;
   // Splitting pays when the launch has at most one wave per SIMD (1024 on
-  // 256 CUs) and every split keeps at least 2048 keys, or 1024 for blocks of
-  // at most 64 query rows (decoding-like): then aim for four waves per SIMD.
-  // Measured on MI355X: one query row per head against 16K keys runs 4x
-  // faster with 8 splits, and 16 gain another 16% (33.6 -> 28.2 us at B1
-  // H16 D64; B1 H8 N_k=32768 D128: 52.2 -> 43.7 us with 32 instead of 16);
-  // B1 H2 N16384 causal 1.7x with 4; launches with more waves, or short key
-  // ranges (B2 H12 N512 or N2048), gain nothing because the partial results
+  // 256 CUs): aim for four waves per SIMD with splits of at least 2048
+  // keys.  Where that still leaves fewer than 1024 waves, splits down to
+  // 1024 keys fill up to 1024 waves.  Measured on MI355X (bf16, us, S =
+  // splits): B1 H8 N_q=128 N_k=32768 D128 causal S16 49.5, S32 35.2; B1 H12
+  // N_q=512 N_k=4096 D64 S2 31.9, S4 23.7; B1 H16 N_q=512 N_k=16384 D64
+  // causal S8 57.7, S16 62.8; B1 H32 N_q=512 N_k=8192 D128 causal S4 95.3,
+  // S8 101.5; B1 H16 N_q=2048 N_k=16384 D64 causal S2 181.5, S4 173.9; B1
+  // H2 N16384 causal 1.7x with 4.  Square launches of one wave per SIMD
+  // (B2 H8 N2048, B2 H12 N512) gain nothing, because the partial results
   // cost a pass over O in fp32.
   if (waves > 1024) return 1;
   int64_t s = (4096 + waves - 1) / waves;
-  const int min_keys = Nq <= 64 ? 1024 : 2048;
-  s = s < Nk / min_keys ? s : Nk / min_keys;
   s = s < 64 ? s : 64;
+  const int64_t s2048 = s < Nk / 2048 ? s : Nk / 2048;
+  if (waves * (s2048 > 1 ? s2048 : 1) >= 1024) {
+    s = s2048;
+  } else {
+    const int64_t fill = (1024 + waves - 1) / waves;
+    s = s < Nk / 1024 ? s : Nk / 1024;
+    s = s < fill ? s : fill;
+  }
   return s > 1 ? static_cast<int>(s) : 1;
 }
 

@@ -330,11 +330,18 @@ def test_split_entry_points_without_launch():
     assert lib.fa_fwd_split_count(2, 12, 512, 512, 64, 0) == 1
     assert lib.fa_fwd_split_count(1, 8, 4096, 4096, 128, 1) == 1
     assert lib.fa_fwd_split_count(1, 2, 16384, 16384, 64, 1) == 4
-    # Blocks of at most 64 query rows split down to 1024 keys, longer ones
-    # to 2048.
+    # Splits of at least 2048 keys towards four waves per SIMD; where those
+    # leave fewer than 1024 waves, splits down to 1024 keys up to 1024 waves.
     assert lib.fa_fwd_split_count(1, 16, 64, 16384, 64, 1) == 16
-    assert lib.fa_fwd_split_count(1, 16, 65, 16384, 64, 1) == 8
+    assert lib.fa_fwd_split_count(1, 16, 65, 16384, 64, 1) == 16
     assert lib.fa_fwd_split_count(1, 16, 3, 16384, 64, 1) == 16
+    assert lib.fa_fwd_split_count(1, 8, 128, 32768, 128, 1) == 32
+    assert lib.fa_fwd_split_count(1, 12, 512, 4096, 64, 0) == 4
+    assert lib.fa_fwd_split_count(1, 16, 512, 16384, 64, 1) == 8
+    assert lib.fa_fwd_split_count(1, 32, 512, 8192, 128, 1) == 4
+    assert lib.fa_fwd_split_count(1, 16, 2048, 16384, 64, 1) == 4
+    assert lib.fa_fwd_split_count(2, 8, 2048, 2048, 64, 0) == 1
+    assert lib.fa_fwd_split_count(1, 8, 2048, 2048, 64, 0) == 2
     # One or two rows (the vector-unit kernel): 256 workgroups of at least
     # 1024 keys, none once B*H reaches 256.
     assert lib.fa_fwd_split_count(1, 16, 1, 16384, 64, 1) == 16
