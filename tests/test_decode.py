@@ -99,8 +99,7 @@ def test_decode_long_history_all_heads():
     """One new token per head against 16K keys, 16 heads, the automatic
     split count, every head against the oracle."""
     _say("case decode B1 H16 Nk16384")
-    from io_aware_exact_02_amd import _lib as L
-    assert L.load().fa_fwd_split_count(1, 16, 1, 16384, 64, 1) > 1
+    assert _lib.load().fa_fwd_split_count(1, 16, 1, 16384, 64, 1) > 1
     inp = _inputs(1, 1, 16384, 16, 64, "bf16", 9950)
     dev = torch.device("cuda")
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
@@ -202,3 +201,39 @@ def test_three_rows_take_the_tiled_kernels():
     O, LSE = oa.attention_forward(inp["q"], inp["k"], inp["v"], causal=True)
     _check(_f64(o3), _f64(lse3), O, LSE, "3 rows")
     _check(_f64(o2), _f64(lse2), O[:, 1:], LSE[:, :, 1:], "last 2 rows")
+
+
+def test_decode_graph_replay_matches_eager():
+    """The decode forward captured in a HIP graph, split (partials, then the
+    merge) and unsplit: every replay, with stale outputs and eager work in
+    between, equals the eager result bit for bit."""
+    _say("case decode graph replay")
+    dev = torch.device("cuda")
+    a = _inputs(2, 2, 3000, 3, 128, "bf16", 9997)
+    b = _inputs(3, 1, 2000, 4, 64, "f16", 9998)
+    qa, ka, va = (a[n].to(dev) for n in ("q", "k", "v"))
+    qb, kb, vb = (b[n].to(dev) for n in ("q", "k", "v"))
+    oa_e, la_e = fa.fwd(qa, ka, va, causal=True, num_splits=6)
+    ob_e, lb_e = fa.fwd(qb, kb, vb, causal=False, num_splits=1)
+    torch.cuda.synchronize()
+    oa_, la_ = torch.empty_like(oa_e), torch.empty_like(la_e)
+    ob_, lb_ = torch.empty_like(ob_e), torch.empty_like(lb_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fa.fwd(qa, ka, va, causal=True, num_splits=6, out=oa_, lse=la_)
+        fa.fwd(qb, kb, vb, causal=False, num_splits=1, out=ob_, lse=lb_)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fwd(qa, ka, va, causal=True, num_splits=6, out=oa_, lse=la_)
+        fa.fwd(qb, kb, vb, causal=False, num_splits=1, out=ob_, lse=lb_)
+    for rep in range(3):
+        for t in (oa_, la_, ob_, lb_):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oa_, oa_e) and torch.equal(la_, la_e), f"split replay {rep}"
+        assert torch.equal(ob_, ob_e) and torch.equal(lb_, lb_e), f"unsplit replay {rep}"
+        _ = torch.cos(qa.float()).sum()
+        torch.cuda.synchronize()
