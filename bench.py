@@ -79,11 +79,11 @@ def conv_flops(w):
 
 def dq_atomic_adds(w) -> int:
     """Number of 32-bit atomic adds one dK/dV launch issues into the dQ
-    accumulator.  Each workgroup owns a block of keys (256 at head_dim 64,
-    128 at head_dim 128) and adds its dS K contribution for every query row
+    accumulator.  Each workgroup owns a block of 256 keys and adds its
+    dS K contribution for every query row
     from the first one that sees its first key (causal) or from row 0, to
     the last row: D adds per row."""
-    bkv = 256 if w.D == 64 else 128
+    bkv = 256
     total = 0
     for kb0 in range(0, w.N, bkv):
         q_begin = kb0 if w.causal else 0

@@ -153,11 +153,12 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ kernel 2
 //
-// Workgroup = NW wave64s; wave w owns the 32 keys kb0 + 32w .. +31 of the
-// workgroup's key block (BKV = 32*NW keys) and keeps their K and V rows in
-// registers as MFMA B operands, and their dK, dV accumulators.  The
-// workgroup walks the query tiles (64 rows each; causal: only tiles at or
-// after its first key).  Per tile, each wave computes
+// Workgroup = NW wave64s; wave w owns the 32*SUB keys kb0 + 32*SUB*w ..
+// of the workgroup's key block (BKV = 32*SUB*NW keys), in SUB sub-blocks of
+// 32, and keeps their V rows (and, without KLDS, their K rows) in registers
+// as MFMA B operands, and their dK, dV accumulators.  The
+// workgroup walks the query tiles (BQ = 64 or 32 rows each; causal: only
+// tiles at or after its first key).  Per tile, each wave computes
 //   S  = Q K^T, dP = dO V^T           (A: Q / dO rows from LDS)
 //   P  = exp2(S*c - LSE*log2 e),  dS = P o (dP - Dvec)
 //   dV += P^T dO, dK += dS^T Q        (B: dO / Q gathered transposed)
@@ -177,9 +178,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p) {
 // This fills the device in launches with few key blocks, and evens out
 // causal ones, where the first key block's query range is the whole
 // sequence and the last one's one tile.
-template <int D, int NW, int BQ_>
+template <int D, int NW, int BQ_, int SUB_ = 1>
 struct BwdCfg {
-  static constexpr int BKV = 32 * NW;   // keys per workgroup
+  static constexpr int SUB = SUB_;      // 32-key sub-blocks per wave
+  static constexpr int BKV = 32 * SUB * NW;  // keys per workgroup
   static constexpr int BQ = BQ_;        // query rows per tile (32 or 64)
   static constexpr int NQB = BQ / 32;   // 32-row query blocks per tile
   static constexpr int DB = D / 32;     // 32-wide d blocks
@@ -191,20 +193,30 @@ struct BwdCfg {
   static_assert(QPT * THREADS == BQ * CPR, "tile load must divide evenly");
 };
 
-template <typename T, int D, int NW, int BQ_, bool KLDS, bool CAUSAL, bool SEG>
+template <typename T, int D, int NW, int BQ_, int SUB, bool KLDS, bool CAUSAL, bool SEG>
 __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
-  using Cfg = BwdCfg<D, NW, BQ_>;
+  using Cfg = BwdCfg<D, NW, BQ_, SUB>;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NQB = Cfg::NQB, DB = Cfg::DB;
   constexpr int NBLK = Cfg::NBLK, BPW = Cfg::BPW, THREADS = Cfg::THREADS;
   constexpr int CPR = Cfg::CPR, QPT = Cfg::QPT;
   constexpr int KC = D / 16;
   constexpr int QTILE = BQ * D;    // halves per Q (or dO) buffer
   constexpr int STILE = BKV * BQ;  // halves per dS^T buffer
+  // VH (head_dim 128, two sub-blocks): the V rows of each wave's last
+  // sub-block live in LDS (Vs, 32 rows per wave) instead of registers, and
+  // the dS^T tile is single-buffered (one more barrier per tile) to make
+  // room for them.
+#ifndef FA_VH
+#define FA_VH 1
+#endif
+  constexpr bool VH = FA_VH && D == 128 && SUB == 2;
+  constexpr int NST = VH ? 1 : 2;  // dS^T buffers
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[VH ? NW * 32 * D : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2 * QTILE];
   __shared__ __attribute__((aligned(16))) uint16_t dOs[2 * QTILE];
-  __shared__ __attribute__((aligned(16))) uint16_t dSt[2 * STILE];
+  __shared__ __attribute__((aligned(16))) uint16_t dSt[NST * STILE];
   __shared__ __attribute__((aligned(16))) float lse_s[2 * BQ];  // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float ndv_s[2 * BQ];  // -Dvec
 
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const int BH = p.B * p.H;
   const XcdItem wg = xcd_item(blockIdx.x, BH, p.num_kblocks * (SEG ? p.nseg : 1));
   if (!wg.valid) return;
-  poison_lds(Ks, Qs, dOs, dSt, lse_s, ndv_s);
+  poison_lds(Ks, Vs, Qs, dOs, dSt, lse_s, ndv_s);
   const int bh = wg.bh;
   const int item = wg.item;
   const int kblk = SEG ? item / p.nseg : item;
@@ -240,22 +252,26 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t dq_rs = raw_rsrc(dq_acc, N * D * 4);
 
   const int kb0 = kblk * BKV;
-  const int kw0 = kb0 + 32 * wave;
-  const int key = kw0 + l32;  // the key this lane serves in S and dP
+  const int kw0 = kb0 + 32 * SUB * wave;  // this wave's first key
+  // Sub-block sb: the key this lane serves in S and dP is kw0 + 32*sb + l32.
 
   // B operands of S = Q K^T and dP = dO V^T: k / v[key][16*kc + 8*hh + 0..7].
   // With KLDS the K operand is read from the workgroup's K rows in LDS
   // instead (register budget at head_dim 128).
-  u32x4 kreg[KLDS ? 1 : KC], vreg[KC];
+  u32x4 kreg[SUB][KLDS ? 1 : KC], vreg[VH ? SUB - 1 : SUB][KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (key < Nk) {
-      if constexpr (!KLDS) kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + 16 * kc + 8 * hh);
-      vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + 16 * kc + 8 * hh);
+  for (int sb = 0; sb < (VH ? SUB - 1 : SUB); ++sb) {
+    const int key = kw0 + 32 * sb + l32;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < Nk) {
+        if constexpr (!KLDS) kv = ldg16(kbase + static_cast<int64_t>(key) * p.sk.n + 16 * kc + 8 * hh);
+        vv = ldg16(vbase + static_cast<int64_t>(key) * p.sv.n + 16 * kc + 8 * hh);
+      }
+      if constexpr (!KLDS) kreg[sb][kc] = kv;
+      vreg[sb][kc] = vv;
     }
-    if constexpr (!KLDS) kreg[kc] = kv;
-    vreg[kc] = vv;
   }
   // Fixed-point scale of the dQ accumulator for this head (see the file
   // comment), from the preprocess maxima of |dO_i|, |K| and |V_j|:
@@ -310,6 +326,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     if (kk < Nk) kv = ldg16(kbase + static_cast<int64_t>(kk) * p.sk.n + col);
     lds_write16(&Ks[tile_off<D>(row, col)], kv);
   }
+  // VH: the V rows of every wave's last sub-block, wave w's at rows 32w.
+  if constexpr (VH) {
+    for (int c = tid; c < NW * 32 * CPR; c += THREADS) {
+      const int row = c / CPR;
+      const int col = (c % CPR) * 8;
+      const int kk = kb0 + 32 * (SUB * (row / 32) + SUB - 1) + row % 32;
+      u32x4 vv = {0u, 0u, 0u, 0u};
+      if (kk < Nk) vv = ldg16(vbase + static_cast<int64_t>(kk) * p.sv.n + col);
+      lds_write16(&Vs[tile_off<D>(row, col)], vv);
+    }
+  }
 
   // ---- per-lane LDS offsets (bytes), fixed for the whole kernel
   uint32_t q_off[KC];  // row reads of Q / dO (A of S, dP); + 32*qb rows
@@ -320,7 +347,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < DB; ++db) qt_off[t][db] = tr_off<D, true>(lane, t, db);
-  // dS^T rows written by this wave: row 32*wave + l32, query chunk 2*(2qb+c) + hh.
+  // dS^T rows written by this wave: row 32*(SUB*wave + sb) + l32, query chunk
+  // 2*(2qb+c) + hh.
   // The 64-wide dS^T tile uses the store swizzle swz_st (conflict-free
   // 128-bit stores); the 32-wide one keeps swz<32>.
   constexpr bool DS_ST = BQ == 64;
@@ -330,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   } else {
     ds_sw = swz<BQ>(l32);
   }
-  const uint32_t ds_w = static_cast<uint32_t>((32 * wave + l32) * 2 * BQ + 16 * (hh ^ ds_sw));
+  const uint32_t ds_w = static_cast<uint32_t>((32 * SUB * wave + l32) * 2 * BQ + 16 * (hh ^ ds_sw));
   // This wave's dQ blocks: transposed reads of dS (A) and K (B).
   uint32_t s_off[BPW][2], kt_off[BPW][2];
 #pragma unroll
@@ -437,12 +465,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  f32x16 dkacc[DB], dvacc[DB];
+  f32x16 dkacc[SUB][DB], dvacc[SUB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dkacc[db] = (f32x16){};
-    dvacc[db] = (f32x16){};
-  }
+  for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dkacc[sb][db] = (f32x16){};
+      dvacc[sb][db] = (f32x16){};
+    }
 
   // ---- dQ: one 32x32 block per wave per tile, added with integer atomics
   // in units of B / 2^30 (rounded to nearest).
@@ -472,36 +502,57 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // ---- S, dP, P, dS, dV, dK for this wave's 32 keys and one query tile.
-  auto compute = [&](auto bufc, auto maskc, int qt, u32x4 (&pS)[NQB][2]) {
+  // ---- S, dP, P, dS, dV, dK for this wave's 32*SUB keys and one query tile.
+  // The sub-blocks share each operand read from LDS.
+  auto compute = [&](auto bufc, auto maskc, int qt, u32x4 (&pS)[SUB][NQB][2]) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASK = decltype(maskc)::value;
     const uint16_t* qs = Qs + BUF * QTILE;
     const uint16_t* dos = dOs + BUF * QTILE;
     const float* ls = lse_s + BUF * BQ + 8 * hh;
     const float* nd = ndv_s + BUF * BQ + 8 * hh;
-    u32x4 pP[NQB][2];
+    u32x4 pP[SUB][NQB][2];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      // C value i: query qt + 32*qb + c_item(i, hh), key = this lane's key.
-      // dP starts from -Dvec of its query so that the product yields dP - Dvec.
+      // C value i: query qt + 32*qb + c_item(i, hh), key = this lane's key of
+      // sub-block sb.  dP starts from -Dvec of its query so that the product
+      // yields dP - Dvec.
       const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd + 32 * qb);
       const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 32 * qb + 4);
       const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 32 * qb + 16);
       const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 32 * qb + 20);
-      f32x16 dp = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
-                   n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
-      f32x16 s = (f32x16){};
+      f32x16 dp[SUB], s[SUB];
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        dp[sb] = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                          n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+        s[sb] = (f32x16){};
+      }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        u32x4 kop;
-        if constexpr (KLDS) {
-          kop = lds_ld16(Ks + 32 * wave * D, q_off[kc]);  // rows of this wave's keys
-        } else {
-          kop = kreg[kc];
+        const u32x4 aq = lds_ld16(qs + 32 * qb * D, q_off[kc]);
+        const u32x4 ado = lds_ld16(dos + 32 * qb * D, q_off[kc]);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          u32x4 kop;
+          if constexpr (KLDS) {
+            kop = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);  // this sub-block's keys
+          } else {
+            kop = kreg[sb][kc];
+          }
+          s[sb] = mfma32x32x16<T>(aq, kop, s[sb]);
+          u32x4 vop;
+          if constexpr (VH) {
+            if (sb == SUB - 1) {
+              vop = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
+            } else {
+              vop = vreg[sb < SUB - 1 ? sb : 0][kc];
+            }
+          } else {
+            vop = vreg[sb][kc];
+          }
+          dp[sb] = mfma32x32x16<T>(ado, vop, dp[sb]);
         }
-        s = mfma32x32x16<T>(lds_ld16(qs + 32 * qb * D, q_off[kc]), kop, s);
-        dp = mfma32x32x16<T>(lds_ld16(dos + 32 * qb * D, q_off[kc]), vreg[kc], dp);
       }
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * qb);
       const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 4);
@@ -509,27 +560,39 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 20);
       const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
                             l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-      float pv[16], dsv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[i], c_scale, -lv[i]));
-        if constexpr (MASK) {
-          const int q = qt + 32 * qb + c_item(i, hh);
-          const bool valid = key < Nk && (!CAUSAL || key <= q + off);
-          pr = valid ? pr : 0.0f;
+      for (int sb = 0; sb < SUB; ++sb) {
+        const int key = kw0 + 32 * sb + l32;
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c_scale, -lv[i]));
+          if constexpr (MASK) {
+            const int q = qt + 32 * qb + c_item(i, hh);
+            const bool valid = key < Nk && (!CAUSAL || key <= q + off);
+            pr = valid ? pr : 0.0f;
+          }
+          pv[i] = pr;
+          dsv[i] = pr * dp[sb][i];
         }
-        pv[i] = pr;
-        dsv[i] = pr * dp[i];
+        pP[sb][qb][0] = pack8<T>(pv);
+        pP[sb][qb][1] = pack8<T>(pv + 8);
+        pS[sb][qb][0] = pack8<T>(dsv);
+        pS[sb][qb][1] = pack8<T>(dsv + 8);
       }
-      pP[qb][0] = pack8<T>(pv);
-      pP[qb][1] = pack8<T>(pv + 8);
-      pS[qb][0] = pack8<T>(dsv);
-      pS[qb][1] = pack8<T>(dsv + 8);
     }
     // LLVM's MFMA interleaving strategy 1 for the rest of the tile: measured
     // 4-7% faster at head_dim 64, slower at 128.
     if constexpr (D == 64) __builtin_amdgcn_iglp_opt(1);
-    // dV += P^T dO, dK += dS^T Q over the tile's query rows.
+    // Head_dim 128 (one wave per SIMD, the dK/dV accumulators of 64 keys in
+    // the 256 AGPRs): without this barrier the scheduler hoists the LDS reads
+    // of the dV/dK products above the softmax and runs out of registers
+    // (700-900 spilled VGPRs; 2-6 with it in the query-segment and
+    // non-causal forms).  Barriers inside the read loops as well (every 1, 2
+    // or 4 steps) measured within 1% of this alone.
+    if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
+    // dV += P^T dO, dK += dS^T Q over the tile's query rows; each operand
+    // read from LDS serves every sub-block.
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
@@ -538,9 +601,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x4 bdo = lds_tr16(dos + r * D, qt_off[0][db], qt_off[1][db]);
-          dvacc[db] = mfma32x32x16<T>(pP[qb][c], bdo, dvacc[db]);
+#pragma unroll
+          for (int sb = 0; sb < SUB; ++sb)
+            dvacc[sb][db] = mfma32x32x16<T>(pP[sb][qb][c], bdo, dvacc[sb][db]);
           const u32x4 bq = lds_tr16(qs + r * D, qt_off[0][db], qt_off[1][db]);
-          dkacc[db] = mfma32x32x16<T>(pS[qb][c], bq, dkacc[db]);
+#pragma unroll
+          for (int sb = 0; sb < SUB; ++sb)
+            dkacc[sb][db] = mfma32x32x16<T>(pS[sb][qb][c], bq, dkacc[sb][db]);
         }
       }
     }
@@ -553,9 +620,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     if (has_next) load_tile(t + 1);
     if (t > 0) dq_atomics(qt - BQ);
 
-    u32x4 pS[NQB][2];
+    u32x4 pS[SUB][NQB][2];
     if (!CAUSAL || qt + BQ - 1 + off >= kw0) {
-      const bool need_mask = (CAUSAL && kw0 + 31 > qt + off) || (kw0 + 31 >= Nk);
+      // A sub-block whose keys all lie after the tile's queries is computed
+      // under the mask too: its P and dS are exactly 0.
+      const bool need_mask =
+          (CAUSAL && kw0 + 32 * SUB - 1 > qt + off) || (kw0 + 32 * SUB - 1 >= Nk);
       if (need_mask) {
         compute(bufc, IntC<1>{}, qt, pS);
       } else {
@@ -563,20 +633,28 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       }
     } else {  // causal: every key of this wave lies after every query of the tile
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) pS[qb][0] = pS[qb][1] = (u32x4){0u, 0u, 0u, 0u};
+      for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) pS[sb][qb][0] = pS[sb][qb][1] = (u32x4){0u, 0u, 0u, 0u};
     }
     // dS^T (as rounded for the MFMAs) to LDS: row = key, query columns.
-    uint16_t* dst = dSt + BUF * STILE;
+    // Single-buffered (VH): every wave has finished the previous tile's dQ
+    // reads of it first.
+    if constexpr (VH) __syncthreads();
+    uint16_t* dst = dSt + (VH ? 0 : BUF * STILE);
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
+    for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) lds_st16(dst, ds_w ^ (64 * qb + 32 * c), pS[qb][c]);
-    }
+      for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          lds_st16(dst + 32 * sb * BQ, ds_w ^ (64 * qb + 32 * c), pS[sb][qb][c]);
+      }
     if (has_next) store_tile(IntC<BUF ^ 1>{});
     __syncthreads();
 
     // dQ(tile) = dS K over the workgroup's keys.
-    const uint16_t* sts = dSt + BUF * STILE;
+    const uint16_t* sts = dSt + (VH ? 0 : BUF * STILE);
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       f32x16 acc = (f32x16){};
@@ -608,46 +686,60 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // fp32 sums go to the workspace: partial sums [seg][bh][key][d].
   if constexpr (!SEG) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = kw0 + c_row(i, hh);
-        if (kk < Nk) {
-          const int d = 32 * db + l32;
-          p.dk[b * p.sdk.b + static_cast<int64_t>(kk) * p.sdk.n + h * p.sdk.h + d] =
-              to_half_bits<T>(dkacc[db][i] * p.scale);
-          p.dv[b * p.sdv.b + static_cast<int64_t>(kk) * p.sdv.n + h * p.sdv.h + d] =
-              to_half_bits<T>(dvacc[db][i]);
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = kw0 + 32 * sb + c_row(i, hh);
+          if (kk < Nk) {
+            const int d = 32 * db + l32;
+            p.dk[b * p.sdk.b + static_cast<int64_t>(kk) * p.sdk.n + h * p.sdk.h + d] =
+                to_half_bits<T>(dkacc[sb][db][i] * p.scale);
+            p.dv[b * p.sdv.b + static_cast<int64_t>(kk) * p.sdv.n + h * p.sdv.h + d] =
+                to_half_bits<T>(dvacc[sb][db][i]);
+          }
         }
       }
-    }
   } else {
     const int64_t base = (static_cast<int64_t>(seg) * BH + bh) * Nk;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = kw0 + c_row(i, hh);
-        if (kk < Nk) {
-          const int64_t e = (base + kk) * D + 32 * db + l32;
-          p.dk_part[e] = dkacc[db][i];
-          p.dv_part[e] = dvacc[db][i];
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = kw0 + 32 * sb + c_row(i, hh);
+          if (kk < Nk) {
+            const int64_t e = (base + kk) * D + 32 * db + l32;
+            p.dk_part[e] = dkacc[sb][db][i];
+            p.dv_part[e] = dvacc[sb][db][i];
+          }
         }
       }
-    }
   }
 }
 
-// dK/dV kernel shape per head_dim.  Keys per workgroup (32 per wave) set the
-// number of dQ atomics: each dQ element receives one per key block.  At
-// head_dim 64, 8 waves (256 keys) fit in 256 registers per wave; at head_dim
-// 128 the dK/dV accumulators of 4 waves (128 keys) already take half of them.
+// dK/dV kernel shape per head_dim.  Keys per workgroup set the number of dQ
+// atomics: each dQ element receives one per key block, and these atomics
+// bound the backward.  Both head dims take 256 keys per workgroup:
+//   head_dim 64:  8 waves of 32 keys, 64-row query tiles, two waves per SIMD
+//                 (dK/dV accumulators 64 registers per wave);
+//   head_dim 128: 4 waves of 64 keys (two sub-blocks of 32), 32-row query
+//                 tiles, one wave per SIMD: the dK/dV accumulators fill the
+//                 256 AGPRs, V stays in registers and K is read from LDS
+//                 (64 KB; K is in LDS for dQ anyway); LDS 129 KB.
+// Measured at head_dim 128 against 4 waves of 32 keys (128 keys, 64-row
+// tiles, K and V in registers; in-process A/B on one box): B1 H8 N8192
+// causal backward 0.735 -> 0.621 ms (half the dQ atomics), B1 H2 N16384
+// causal 0.750 -> 0.603 ms, B2 H12 N2048 non-causal 0.338 -> 0.316 ms.
 template <int D>
 struct BwdShape {
   static constexpr int NW = D == 64 ? 8 : 4;
-  static constexpr int BQ = 64;
-  static constexpr bool KLDS = false;
-  static constexpr int BKV = BwdCfg<D, NW, BQ>::BKV;
+  static constexpr int BQ = D == 64 ? 64 : 32;
+  static constexpr int SUB = D == 64 ? 1 : 2;
+  static constexpr bool KLDS = D != 64;
+  static constexpr int BKV = BwdCfg<D, NW, BQ, SUB>::BKV;
 };
 
 // Query segments per key block (BwdParams nseg): enough for about 512
@@ -761,10 +853,10 @@ static hipError_t launch_bwd_t(const BwdParams& p_in, unsigned stages, hipStream
   if (stages & 2u) {
     const int64_t blocks = xcd_grid(p.B * p.H, p.num_kblocks * p.nseg);
     if (p.nseg > 1) {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, true>),
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::SUB, Sh::KLDS, CAUSAL, true>),
                          dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::KLDS, CAUSAL, false>),
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, NW, Sh::BQ, Sh::SUB, Sh::KLDS, CAUSAL, false>),
                          dim3(static_cast<unsigned>(blocks)), dim3(64 * NW), 0, s, p);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;

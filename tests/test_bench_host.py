@@ -31,7 +31,7 @@ def _atomics_by_rows(w):
     """Count row by row: a query row r takes D atomic adds from every key
     block whose first key it sees (causal: first key <= r; otherwise every
     block), the dQ elements of that row."""
-    bkv = 256 if w.D == 64 else 128
+    bkv = 256
     blocks = (w.N + bkv - 1) // bkv
     total = 0
     for r in range(w.N):
@@ -53,7 +53,7 @@ def test_dq_atomic_count(w):
 def test_dq_atomic_count_values():
     """The counts quoted for the two causal sweep workloads."""
     assert bench.dq_atomic_adds(WORKLOADS["c5"]) == 545_259_520
-    assert bench.dq_atomic_adds(WORKLOADS["c4"]) == 272_629_760
+    assert bench.dq_atomic_adds(WORKLOADS["c4"]) == 138_412_032
 
 
 def test_refuses_several_gpus():

@@ -51,15 +51,15 @@ def test_workspace_bytes_is_linear_in_n():
 
     # Dvec, the int32 dQ accumulator, three maxima per 16-row block, one
     # fixed-point bound per head, and -- for launches with fewer than 512 key
-    # blocks (256 keys at head_dim 64, 128 at head_dim 128), whose query
-    # range a causal mask splits into S = min(8, ceil(512 / blocks),
-    # ceil(N / 64)) segments -- S fp32 partial dK and dV sums: O(N*D) per
-    # head, no N*N term.
+    # blocks (256 keys), whose query range a causal mask splits into
+    # S = min(8, ceil(512 / blocks), query tiles) segments (tiles of 64 rows
+    # at head_dim 64, 32 at head_dim 128) -- S fp32 partial dK and dV sums:
+    # O(N*D) per head, no N*N term.
     def want_bytes(B, H, N, D):
         heads, rows = B * H, B * H * N
-        bkv = 256 if D == 64 else 128
+        bkv, bq = 256, (64 if D == 64 else 32)
         blocks = heads * ((N + bkv - 1) // bkv)
-        segs = min(8, -(-512 // blocks), -(-N // 64)) if blocks < 512 else 1
+        segs = min(8, -(-512 // blocks), -(-N // bq)) if blocks < 512 else 1
         part = 2 * a256(4 * segs * heads * N * D) if segs > 1 else 0
         return (a256(4 * rows) + a256(4 * rows * D)
                 + a256(4 * 3 * heads * ((N + 15) // 16)) + a256(4 * heads) + part)
@@ -407,11 +407,17 @@ def test_noalloc_rejects_before_launch():
     assert call(causal=2) == _lib.FA_ERR_INVALID_ARG
     assert call(scale=float("nan")) == _lib.FA_ERR_INVALID_ARG
     assert call(B=0) == _lib.FA_ERR_INVALID_ARG
-    # Largest N whose scratch fits, and the next size up.
-    fits = [n for n in (8192, 16384) if lib.fa_bwd_qk_workspace_bytes(1, 8, n, n, 128) <= cap]
+    # Largest N whose non-causal scratch fits, and the next size up.
+    fits = [n for n in (8192, 16384)
+            if lib.fa_bwd_qk_workspace_bytes_for(1, 8, n, n, 128, 0) <= cap]
     assert fits == [8192]
     assert call(B=1, H=16, Nq=16384, Nk=16384, D=64, causal=1) == _lib.FA_ERR_TOO_LARGE
     assert call(B=1, H=8, Nq=16384, Nk=16384, D=128) == _lib.FA_ERR_TOO_LARGE
+    # The causal B1 H8 N8192 D128 backward splits its 32 key blocks per head
+    # into 2 query segments, whose fp32 partial dK, dV sums (128 MiB) exceed
+    # the array.
+    assert lib.fa_bwd_qk_workspace_bytes_for(1, 8, 8192, 8192, 128, 1) > cap
+    assert call(B=1, H=8, Nq=8192, Nk=8192, D=128, causal=1) == _lib.FA_ERR_TOO_LARGE
     assert b"TOO_LARGE" in lib.fa_status_str(_lib.FA_ERR_TOO_LARGE)
 
 

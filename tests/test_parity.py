@@ -226,10 +226,10 @@ def test_snake_order_grids(B, H, N, D):
     (1, 7, 4000, 64, True, 5),     # 112 key blocks, ragged tail
     (1, 12, 4096, 64, True, 3),    # 192 key blocks
     (3, 2, 200, 64, True, 4),      # 6 key blocks, capped by the 4 query tiles
-    (1, 2, 2048, 128, True, 8),    # 32 key blocks
-    (1, 8, 2048, 128, True, 4),    # 128 key blocks
+    (1, 2, 2048, 128, True, 8),    # 16 key blocks
+    (1, 16, 2048, 128, True, 4),   # 128 key blocks
     (1, 1, 4096, 64, False, 8),    # 16 key blocks
-    (2, 3, 1000, 128, False, 6),   # 48 key blocks, ragged tail
+    (2, 6, 1000, 128, False, 6),   # 48 key blocks, ragged tail
     (1, 4, 8192, 64, False, 2),    # 128 key blocks
     (1, 12, 4096, 64, False, 1),   # 192 key blocks: unsplit
 ])
@@ -240,12 +240,12 @@ def test_query_segment_counts(B, H, N, D, causal, segs):
     tiles), non-causal ones at 128 or fewer with min(8, ceil(256 / blocks),
     query tiles).  Every output against the oracle, in full."""
     what = f"segments B={B} H={H} N={N} D={D} causal={causal}"
-    bkv = 256 if D == 64 else 128
+    bkv, bq = 256, (64 if D == 64 else 32)
     blocks = B * H * -(-N // bkv)
     if causal:
-        want = min(8, -(-512 // blocks), -(-N // 64)) if blocks < 512 else 1
+        want = min(8, -(-512 // blocks), -(-N // bq)) if blocks < 512 else 1
     else:
-        want = min(8, -(-256 // blocks), -(-N // 64)) if blocks <= 128 else 1
+        want = min(8, -(-256 // blocks), -(-N // bq)) if blocks <= 128 else 1
     assert want == segs, what
     _say("case", what, "S =", segs)
     inp = random_qkv(B, N, H, D, "bf16", seed=8100 + N + H)
