@@ -211,6 +211,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 #endif
   constexpr bool VH = FA_VH && D == 128 && SUB == 2;
   constexpr int NST = VH ? 1 : 2;  // dS^T buffers
+  // PIPE: the software-pipelined VH loops (compute_vh, and the dQ loop), for
+  // causal launches.  Measured against the plain loops (in-process A/B on one
+  // box): causal B1 H8 N8192 backward 0.591 -> 0.561 ms, B1 H16 N8192 1.17
+  // -> 1.04 ms, B1 H2 N16384 0.571 -> 0.541 ms; non-causal B2 H12 N2048
+  // 0.273 -> 0.310 ms (its form spills more registers), so not there.
+  constexpr bool PIPE = CAUSAL;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[VH ? NW * 32 * D : 8];
@@ -613,6 +619,106 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
+  // ---- The VH form of the tile computation, software-pipelined: with one
+  // wave per SIMD nothing else hides the LDS latency, so each loop issues
+  // the operand reads of its next step (two register slots) before the
+  // MFMAs of the current one, and sched_barrier fixes that order.
+  auto compute_vh = [&](auto bufc, auto maskc, int qt, u32x4 (&pS)[SUB][NQB][2]) {
+    static_assert(VH && NQB == 1 && KLDS, "head_dim 128, 32-row tiles");
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr bool MASK = decltype(maskc)::value;
+    const uint16_t* qs = Qs + BUF * QTILE;
+    const uint16_t* dos = dOs + BUF * QTILE;
+    const float* ls = lse_s + BUF * BQ + 8 * hh;
+    const float* nd = ndv_s + BUF * BQ + 8 * hh;
+    f32x16 s[SUB], dp[SUB];
+    {
+      // dP starts from -Dvec of its query so that the product yields dP - Dvec.
+      const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
+      const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
+      const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
+      const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        dp[sb] = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                          n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+        s[sb] = (f32x16){};
+      }
+    }
+    // Phase A: S = Q K^T, dP = dO V^T over the 8 head_dim chunks.
+    u32x4 aq[2], ado[2], ak[2][SUB], av[2];
+    auto read_a = [&](int kc, int slot) {
+      aq[slot] = lds_ld16(qs, q_off[kc]);
+      ado[slot] = lds_ld16(dos, q_off[kc]);
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) ak[slot][sb] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);
+      av[slot] = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
+    };
+    read_a(0, 0);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int cur = kc & 1;
+      if (kc + 1 < KC) read_a(kc + 1, cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        s[sb] = mfma32x32x16<T>(aq[cur], ak[cur][sb], s[sb]);
+        dp[sb] = mfma32x32x16<T>(ado[cur], sb == SUB - 1 ? av[cur] : vreg[0][kc], dp[sb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Phase C's first operands and the LSE, issued ahead of the softmax.
+    u32x4 bdo[2], bq[2];
+    auto read_c = [&](int j, int slot) {
+      const int c = j / DB, db = j % DB;
+      bdo[slot] = lds_tr16(dos + 16 * c * D, qt_off[0][db], qt_off[1][db]);
+      bq[slot] = lds_tr16(qs + 16 * c * D, qt_off[0][db], qt_off[1][db]);
+    };
+    read_c(0, 0);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
+    const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
+    const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
+                          l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
+    // Phase B: P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded.
+    u32x4 pP[SUB][2];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int key = kw0 + 32 * sb + l32;
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c_scale, -lv[i]));
+        if constexpr (MASK) {
+          const int q = qt + c_item(i, hh);
+          const bool valid = key < Nk && (!CAUSAL || key <= q + off);
+          pr = valid ? pr : 0.0f;
+        }
+        pv[i] = pr;
+        dsv[i] = pr * dp[sb][i];
+      }
+      pP[sb][0] = pack8<T>(pv);
+      pP[sb][1] = pack8<T>(pv + 8);
+      pS[sb][0][0] = pack8<T>(dsv);
+      pS[sb][0][1] = pack8<T>(dsv + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase C: dV += P^T dO, dK += dS^T Q; step j = (16-row half c, d block db).
+#pragma unroll
+    for (int j = 0; j < 2 * DB; ++j) {
+      const int c = j / DB, db = j % DB, cur = j & 1;
+      if (j + 1 < 2 * DB) read_c(j + 1, cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        dvacc[sb][db] = mfma32x32x16<T>(pP[sb][c], bdo[cur], dvacc[sb][db]);
+        dkacc[sb][db] = mfma32x32x16<T>(pS[sb][0][c], bq[cur], dkacc[sb][db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   auto step = [&](auto bufc, int t) {
     constexpr int BUF = decltype(bufc)::value;
     const int qt = q_begin + t * BQ;
@@ -626,10 +732,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       // under the mask too: its P and dS are exactly 0.
       const bool need_mask =
           (CAUSAL && kw0 + 32 * SUB - 1 > qt + off) || (kw0 + 32 * SUB - 1 >= Nk);
-      if (need_mask) {
-        compute(bufc, IntC<1>{}, qt, pS);
+      if constexpr (VH && PIPE) {
+        if (need_mask) {
+          compute_vh(bufc, IntC<1>{}, qt, pS);
+        } else {
+          compute_vh(bufc, IntC<0>{}, qt, pS);
+        }
       } else {
-        compute(bufc, IntC<0>{}, qt, pS);
+        if (need_mask) {
+          compute(bufc, IntC<1>{}, qt, pS);
+        } else {
+          compute(bufc, IntC<0>{}, qt, pS);
+        }
       }
     } else {  // causal: every key of this wave lies after every query of the tile
 #pragma unroll
@@ -655,6 +769,26 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 
     // dQ(tile) = dS K over the workgroup's keys.
     const uint16_t* sts = dSt + (VH ? 0 : BUF * STILE);
+    if constexpr (VH && PIPE) {
+      // One 32x32 block per wave, pipelined like compute_vh.
+      static_assert(BPW == 1 && NBLK == NW, "one dQ block per wave");
+      f32x16 acc = (f32x16){};
+      u32x4 a[2], bk[2];
+      auto read_d = [&](int ks, int slot) {
+        a[slot] = lds_tr16(sts + 16 * ks * BQ, s_off[0][0], s_off[0][1]);
+        bk[slot] = lds_tr16(Ks + 16 * ks * D, kt_off[0][0], kt_off[0][1]);
+      };
+      read_d(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < BKV / 16; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < BKV / 16) read_d(ks + 1, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32x32x16<T>(a[cur], bk[cur], acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dqacc[0] = acc;
+    } else {
 #pragma unroll
     for (int bi = 0; bi < BPW; ++bi) {
       f32x16 acc = (f32x16){};
@@ -667,6 +801,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
       dqacc[bi] = acc;
+    }
     }
   };
 
