@@ -414,43 +414,27 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   u32x4 pf_q[QPT], pf_do[QPT];
   float pf_lse = 0.0f, pf_ndv = 0.0f;
   bool pf_pad = false;
-  // Head_dim 64: every load is unconditional -- rows past N read row N-1
-  // instead, and their LSE is made +inf in store_tile, so their P, dS and
-  // every contribution are exactly 0.  (A load under a branch needs its zero
+  // Every load is unconditional -- rows past N read row N-1 instead, and
+  // their LSE is made +inf in store_tile, so their P, dS and every
+  // contribution are exactly 0.  (A load under a branch needs its zero
   // default written first, and the wait that write takes on the destination
   // registers also drains the previous tile's dQ atomics.)  The LSE and Dvec
   // are scaled and negated in store_tile, after the tile's compute, so
   // nothing waits for them here.  3% faster on the B=1 H=16 N=16384 causal
-  // dK/dV kernel; 2% slower at head_dim 128, which keeps the branch.
+  // dK/dV kernel.
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int it = 0; it < QPT; ++it) {
-      if constexpr (D == 64) {
-        const int col = (tid + THREADS * it) % CPR * 8;
-        const bool in = ld_row[it] + t * BQ < N;
-        pf_q[it] = ldg16(in ? qptr[it] + t * q_step : q_lastrow + col);
-        pf_do[it] = ldg16(in ? doptr[it] + t * do_step : do_lastrow + col);
-      } else {
-        u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
-        if (ld_row[it] + t * BQ < N) {
-          qv = ldg16(qptr[it] + t * q_step);
-          dv = ldg16(doptr[it] + t * do_step);
-        }
-        pf_q[it] = qv;
-        pf_do[it] = dv;
-      }
+      const int col = (tid + THREADS * it) % CPR * 8;
+      const bool in = ld_row[it] + t * BQ < N;
+      pf_q[it] = ldg16(in ? qptr[it] + t * q_step : q_lastrow + col);
+      pf_do[it] = ldg16(in ? doptr[it] + t * do_step : do_lastrow + col);
     }
     if (tid < BQ) {
       const int q = q_begin + t * BQ + tid;
-      if constexpr (D == 64) {
-        pf_pad = q >= N;
-        pf_lse = lse_row[min(q, N - 1)];
-        pf_ndv = dvec_row[min(q, N - 1)];
-      } else {
-        pf_pad = false;
-        pf_lse = q < N ? lse_row[q] * kLog2e : INFINITY;  // padded rows: P = 0
-        pf_ndv = q < N ? -dvec_row[q] : 0.0f;
-      }
+      pf_pad = q >= N;
+      pf_lse = lse_row[min(q, N - 1)];
+      pf_ndv = dvec_row[min(q, N - 1)];
     }
   };
   auto store_tile = [&](auto bufc) {
@@ -461,13 +445,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       lds_st16(dOs + BUF * QTILE, st_off[it], pf_do[it]);
     }
     if (tid < BQ) {
-      if constexpr (D == 64) {
-        lse_s[BUF * BQ + tid] = pf_pad ? INFINITY : pf_lse * kLog2e;  // padded rows: P = 0
-        ndv_s[BUF * BQ + tid] = pf_pad ? 0.0f : -pf_ndv;
-      } else {
-        lse_s[BUF * BQ + tid] = pf_lse;
-        ndv_s[BUF * BQ + tid] = pf_ndv;
-      }
+      lse_s[BUF * BQ + tid] = pf_pad ? INFINITY : pf_lse * kLog2e;  // padded rows: P = 0
+      ndv_s[BUF * BQ + tid] = pf_pad ? 0.0f : -pf_ndv;
     }
   };
 
@@ -631,77 +610,143 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     const uint16_t* dos = dOs + BUF * QTILE;
     const float* ls = lse_s + BUF * BQ + 8 * hh;
     const float* nd = ndv_s + BUF * BQ + 8 * hh;
-    f32x16 s[SUB], dp[SUB];
-    {
-      // dP starts from -Dvec of its query so that the product yields dP - Dvec.
-      const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
-      const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
-      const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
-      const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
-#pragma unroll
-      for (int sb = 0; sb < SUB; ++sb) {
-        dp[sb] = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
-                          n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
-        s[sb] = (f32x16){};
-      }
-    }
-    // Phase A: S = Q K^T, dP = dO V^T over the 8 head_dim chunks.
-    u32x4 aq[2], ado[2], ak[2][SUB], av[2];
-    auto read_a = [&](int kc, int slot) {
-      aq[slot] = lds_ld16(qs, q_off[kc]);
-      ado[slot] = lds_ld16(dos, q_off[kc]);
-#pragma unroll
-      for (int sb = 0; sb < SUB; ++sb) ak[slot][sb] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);
-      av[slot] = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
-    };
-    read_a(0, 0);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int cur = kc & 1;
-      if (kc + 1 < KC) read_a(kc + 1, cur ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int sb = 0; sb < SUB; ++sb) {
-        s[sb] = mfma32x32x16<T>(aq[cur], ak[cur][sb], s[sb]);
-        dp[sb] = mfma32x32x16<T>(ado[cur], sb == SUB - 1 ? av[cur] : vreg[0][kc], dp[sb]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Phase C's first operands and the LSE, issued ahead of the softmax.
+    u32x4 pP[SUB][2];
     u32x4 bdo[2], bq[2];
     auto read_c = [&](int j, int slot) {
       const int c = j / DB, db = j % DB;
       bdo[slot] = lds_tr16(dos + 16 * c * D, qt_off[0][db], qt_off[1][db]);
       bq[slot] = lds_tr16(qs + 16 * c * D, qt_off[0][db], qt_off[1][db]);
     };
-    read_c(0, 0);
-    const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
-    const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
-    const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
-    const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
-    const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
-                          l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-    // Phase B: P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded.
-    u32x4 pP[SUB][2];
+    // Measured (in-process A/B on one box): the query-segment form is
+    // faster with phase A unpipelined and its sub-blocks in turn (B1 H8
+    // N8192 causal backward 0.576 -> 0.547 ms, B1 H2 N16384 0.558 -> 0.527
+    // ms: the pipelined phase A spills registers there), the unsegmented
+    // form with both sub-blocks' phase A pipelined together (B1 H16 N8192
+    // 1.13 -> 1.09 ms).
+    if constexpr (SEG) {
+      // SEG: phases A (S = Q K^T, dP = dO V^T - Dvec, not pipelined) and B
+      // (P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded) one
+      // sub-block at a time, two accumulation chains live instead of four.
 #pragma unroll
-    for (int sb = 0; sb < SUB; ++sb) {
-      const int key = kw0 + 32 * sb + l32;
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c_scale, -lv[i]));
-        if constexpr (MASK) {
-          const int q = qt + c_item(i, hh);
-          const bool valid = key < Nk && (!CAUSAL || key <= q + off);
-          pr = valid ? pr : 0.0f;
+      for (int sb = 0; sb < SUB; ++sb) {
+        f32x16 sacc, dacc;
+        {
+          // dP starts from -Dvec of its query so that the product yields dP - Dvec.
+          const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
+          const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
+          const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
+          const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
+          dacc = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                          n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+          sacc = (f32x16){};
         }
-        pv[i] = pr;
-        dsv[i] = pr * dp[sb][i];
+        u32x4 aq[1], ado[1], ak[1], av[1];
+        auto read_a = [&](int kc, int slot) {
+          aq[slot] = lds_ld16(qs, q_off[kc]);
+          ado[slot] = lds_ld16(dos, q_off[kc]);
+          ak[slot] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);
+          if (sb == SUB - 1) av[slot] = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
+        };
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          read_a(kc, 0);
+          sacc = mfma32x32x16<T>(aq[0], ak[0], sacc);
+          dacc = mfma32x32x16<T>(ado[0], sb == SUB - 1 ? av[0] : vreg[0][kc], dacc);
+        }
+        // The last sub-block issues phase C's first operands ahead of its
+        // softmax work.
+        if (sb == SUB - 1) read_c(0, 0);
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
+        const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
+        const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
+                              l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
+        const int key = kw0 + 32 * sb + l32;
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[i], c_scale, -lv[i]));
+          if constexpr (MASK) {
+            const int q = qt + c_item(i, hh);
+            const bool valid = key < Nk && (!CAUSAL || key <= q + off);
+            pr = valid ? pr : 0.0f;
+          }
+          pv[i] = pr;
+          dsv[i] = pr * dacc[i];
+        }
+        pP[sb][0] = pack8<T>(pv);
+        pP[sb][1] = pack8<T>(pv + 8);
+        pS[sb][0][0] = pack8<T>(dsv);
+        pS[sb][0][1] = pack8<T>(dsv + 8);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      pP[sb][0] = pack8<T>(pv);
-      pP[sb][1] = pack8<T>(pv + 8);
-      pS[sb][0][0] = pack8<T>(dsv);
-      pS[sb][0][1] = pack8<T>(dsv + 8);
+    } else {
+      f32x16 s[SUB], dp[SUB];
+      {
+        // dP starts from -Dvec of its query so that the product yields dP - Dvec.
+        const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
+        const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
+        const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
+        const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          dp[sb] = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+                            n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
+          s[sb] = (f32x16){};
+        }
+      }
+      // Phase A: S = Q K^T, dP = dO V^T over the 8 head_dim chunks.
+      u32x4 aq[2], ado[2], ak[2][SUB], av[2];
+      auto read_a = [&](int kc, int slot) {
+        aq[slot] = lds_ld16(qs, q_off[kc]);
+        ado[slot] = lds_ld16(dos, q_off[kc]);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) ak[slot][sb] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);
+        av[slot] = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
+      };
+      read_a(0, 0);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int cur = kc & 1;
+        if (kc + 1 < KC) read_a(kc + 1, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          s[sb] = mfma32x32x16<T>(aq[cur], ak[cur][sb], s[sb]);
+          dp[sb] = mfma32x32x16<T>(ado[cur], sb == SUB - 1 ? av[cur] : vreg[0][kc], dp[sb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Phase C's first operands and the LSE, issued ahead of the softmax.
+      read_c(0, 0);
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
+      const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
+      const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
+                            l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
+      // Phase B: P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded.
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        const int key = kw0 + 32 * sb + l32;
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c_scale, -lv[i]));
+          if constexpr (MASK) {
+            const int q = qt + c_item(i, hh);
+            const bool valid = key < Nk && (!CAUSAL || key <= q + off);
+            pr = valid ? pr : 0.0f;
+          }
+          pv[i] = pr;
+          dsv[i] = pr * dp[sb][i];
+        }
+        pP[sb][0] = pack8<T>(pv);
+        pP[sb][1] = pack8<T>(pv + 8);
+        pS[sb][0][0] = pack8<T>(dsv);
+        pS[sb][0][1] = pack8<T>(dsv + 8);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase C: dV += P^T dO, dK += dS^T Q; step j = (16-row half c, d block db).
