@@ -217,6 +217,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // -> 1.04 ms, B1 H2 N16384 0.571 -> 0.541 ms; non-causal B2 H12 N2048
   // 0.273 -> 0.310 ms (its form spills more registers), so not there.
   constexpr bool PIPE = CAUSAL;
+  // PIPE64Q: the pipelined dQ loop at head_dim 64 too (in-process A/B,
+  // backward ms: B1 H16 N16384 causal 1.601 -> 1.582, B2 H12 N2048
+  // non-causal 0.098 -> 0.096, B1 H2 N16384 causal 0.240 -> 0.242).  The
+  // pipelined dV/dK loop there was no better than LLVM's interleaving
+  // (1.590 and 1.607 ms at B1 H16 N16384 with and without the dQ one).
+  constexpr bool PIPE64Q = D == 64;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[VH ? NW * 32 * D : 8];
@@ -814,10 +820,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 
     // dQ(tile) = dS K over the workgroup's keys.
     const uint16_t* sts = dSt + (VH ? 0 : BUF * STILE);
-    if constexpr (VH && PIPE) {
-      // One 32x32 block per wave, pipelined like compute_vh.
-      static_assert(BPW == 1 && NBLK == NW, "one dQ block per wave");
+    if constexpr ((VH && PIPE) || (PIPE64Q && BPW == 1)) {
+      // One 32x32 block per wave (or none), pipelined like compute_vh.
+      static_assert(BPW == 1, "one dQ block per wave");
       f32x16 acc = (f32x16){};
+      if (wave < NBLK) {
       u32x4 a[2], bk[2];
       auto read_d = [&](int ks, int slot) {
         a[slot] = lds_tr16(sts + 16 * ks * BQ, s_off[0][0], s_off[0][1]);
@@ -831,6 +838,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         acc = mfma32x32x16<T>(a[cur], bk[cur], acc);
         __builtin_amdgcn_sched_barrier(0);
+      }
       }
       dqacc[0] = acc;
     } else {
