@@ -165,12 +165,12 @@ int fa_fwd_split_count(int B, int H, int Nq, int Nk, int D, int causal);
  * Dvec = rowsum(dO o O) [B, H, N] (fp32), the dQ accumulator [B, H, N, D]
  * (int32, fixed point), three maxima per 16-row block [B*H, 3, ceil(N/16)]
  * (fp32), one dQ bound per head [B*H] (fp32), and -- for launches with
- * few key blocks of 256 (D = 64) or 128 (D = 128) keys, whose query range is
- * split into S segments -- partial dK and dV sums [S, B, H, N, D] (fp32)
- * each.  S = min(8, ceil(512 / key blocks), ceil(N / 64)) for a causal
- * launch with fewer than 512 key blocks, min(8, ceil(256 / key blocks),
- * ceil(N / 64)) for a non-causal one with at most 128, else 1 (no partials
- * when S = 1).  This size is the causal one, which serves either mask.
+ * few key blocks of 256 keys, whose query range is split into S
+ * segments -- partial dK and dV sums [S, B, H, N, D] (fp32) each.
+ * S = min(8, ceil(512 / key blocks), T) for a causal launch with fewer than
+ * 512 key blocks, min(8, ceil(256 / key blocks), T) for a non-causal one
+ * with at most 128, else 1 (no partials when S = 1); T is the number of
+ * query tiles, ceil(N / 64) at D = 64 and ceil(N / 32) at D = 128.  This size is the causal one, which serves either mask.
  * Every part is rounded up to 256 bytes.  O(N*D) per head; no N*N term.
  * Returns 0 for invalid sizes.
  */
@@ -178,7 +178,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int D);
 
 /* Workspace of fa_bwd_qk: as above with Dvec and the dQ accumulator over Nq
  * rows, the maxima over ceil(max(Nq, Nk) / 16) blocks, and the partial sums
- * [S, B, H, Nk, D] with S from the key blocks of Nk and ceil(Nq / 64).
+ * [S, B, H, Nk, D] with S from the key blocks of Nk and the query tiles of
+ * Nq.
  * Like fa_bwd_workspace_bytes, it is the size for a causal launch, which
  * serves either mask. */
 size_t fa_bwd_qk_workspace_bytes(int B, int H, int Nq, int Nk, int D);

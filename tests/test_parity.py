@@ -165,6 +165,21 @@ def test_many_short_heads(D, causal, dtype):
     check_full(inp, causal, what=what)
 
 
+@pytest.mark.parametrize("B,H,N,dtype", [(64, 8, 256, "bf16"), (33, 8, 300, "f16")])
+def test_causal_head_dim_128_unsegmented(B, H, N, dtype):
+    """Causal head_dim-128 backward with at least 512 key blocks of 256 keys,
+    the form that runs without query segments and pipelines its S/dP loop
+    over both 32-key sub-blocks of a wave: 512 heads of 8 full query tiles,
+    and 264 heads of 10 tiles with a ragged tail (528 blocks).  Every output
+    against the oracle."""
+    what = f"causal D=128 unsegmented B={B} H={H} N={N} {dtype}"
+    blocks = B * H * -(-N // 256)
+    assert blocks >= 512, what
+    _say("case", what, "key blocks", blocks)
+    inp = random_qkv(B, N, H, 128, dtype, seed=7230 + N)
+    check_full(inp, True, what=what)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_strided_bhnd_input(D):
     """A [B,H,N,D] tensor passed through a transposed view (strides only)."""
