@@ -205,11 +205,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // VH (head_dim 128, two sub-blocks): the V rows of each wave's last
   // sub-block live in LDS (Vs, 32 rows per wave) instead of registers, and
   // the dS^T tile is single-buffered (one more barrier per tile) to make
-  // room for them.
-#ifndef FA_VH
-#define FA_VH 1
-#endif
-  constexpr bool VH = FA_VH && D == 128 && SUB == 2;
+  // room for them.  The 32 registers this frees removed the spills of the
+  // query-segment form (in-process A/B, backward ms: causal B1 H8 N8192
+  // 0.619 -> 0.596, non-causal B2 H12 N2048 0.317 -> 0.280).
+  constexpr bool VH = D == 128 && SUB == 2;
   constexpr int NST = VH ? 1 : 2;  // dS^T buffers
   // PIPE: the software-pipelined VH loops (compute_vh, and the dQ loop), for
   // causal launches.  Measured against the plain loops (in-process A/B on one
@@ -427,7 +426,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // registers also drains the previous tile's dQ atomics.)  The LSE and Dvec
   // are scaled and negated in store_tile, after the tile's compute, so
   // nothing waits for them here.  3% faster on the B=1 H=16 N=16384 causal
-  // dK/dV kernel.
+  // dK/dV kernel; at head_dim 128 part of the 5% of B=1 H=8 N=8192 causal
+  // (0.561 -> 0.532 ms together with the segment form of compute_vh).
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int it = 0; it < QPT; ++it) {
@@ -618,141 +618,88 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     const float* nd = ndv_s + BUF * BQ + 8 * hh;
     u32x4 pP[SUB][2];
     u32x4 bdo[2], bq[2];
+    // The per-step LDS offsets differ from the first step's by an XOR with a
+    // constant (the chunk swizzle); formed from a per-tile opaque copy, they
+    // cost one VALU op per read instead of 14 registers held all along.
+    uint32_t qo0 = q_off[0], qt0 = qt_off[0][0], qt1 = qt_off[1][0];
+    asm volatile("" : "+v"(qo0), "+v"(qt0), "+v"(qt1));
+    auto qo = [&](int kc) { return qo0 ^ static_cast<uint32_t>(32 * kc); };
     auto read_c = [&](int j, int slot) {
       const int c = j / DB, db = j % DB;
-      bdo[slot] = lds_tr16(dos + 16 * c * D, qt_off[0][db], qt_off[1][db]);
-      bq[slot] = lds_tr16(qs + 16 * c * D, qt_off[0][db], qt_off[1][db]);
+      const uint32_t x = static_cast<uint32_t>(64 * db);
+      bdo[slot] = lds_tr16(dos + 16 * c * D, qt0 ^ x, qt1 ^ x);
+      bq[slot] = lds_tr16(qs + 16 * c * D, qt0 ^ x, qt1 ^ x);
     };
-    // Measured (in-process A/B on one box): the query-segment form is
-    // faster with phase A unpipelined and its sub-blocks in turn (B1 H8
-    // N8192 causal backward 0.576 -> 0.547 ms, B1 H2 N16384 0.558 -> 0.527
-    // ms: the pipelined phase A spills registers there), the unsegmented
-    // form with both sub-blocks' phase A pipelined together (B1 H16 N8192
-    // 1.13 -> 1.09 ms).
-    if constexpr (SEG) {
-      // SEG: phases A (S = Q K^T, dP = dO V^T - Dvec, not pipelined) and B
-      // (P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded) one
-      // sub-block at a time, two accumulation chains live instead of four.
+    // Phases A (S = Q K^T, dP = dO V^T - Dvec) and B (P = exp2(S*c -
+    // LSE*log2 e), dS = P o (dP - Dvec), rounded), both sub-blocks together.
+    // Measured against computing them one sub-block at a time, unpipelined
+    // (in-process A/B, backward ms): causal B1 H8 N8192 0.537 -> 0.517, B1
+    // H16 N8192 1.052 -> 0.963; the two-at-a-time and one-at-a-time
+    // pipelined forms were within 1% of each other.
+    f32x16 s[SUB], dp[SUB];
+    {
+      // dP starts from -Dvec of its query so that the product yields dP - Dvec.
+      const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
+      const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
+      const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
+      const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
 #pragma unroll
       for (int sb = 0; sb < SUB; ++sb) {
-        f32x16 sacc, dacc;
-        {
-          // dP starts from -Dvec of its query so that the product yields dP - Dvec.
-          const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
-          const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
-          const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
-          const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
-          dacc = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
+        dp[sb] = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
                           n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
-          sacc = (f32x16){};
-        }
-        u32x4 aq[1], ado[1], ak[1], av[1];
-        auto read_a = [&](int kc, int slot) {
-          aq[slot] = lds_ld16(qs, q_off[kc]);
-          ado[slot] = lds_ld16(dos, q_off[kc]);
-          ak[slot] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);
-          if (sb == SUB - 1) av[slot] = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
-        };
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          read_a(kc, 0);
-          sacc = mfma32x32x16<T>(aq[0], ak[0], sacc);
-          dacc = mfma32x32x16<T>(ado[0], sb == SUB - 1 ? av[0] : vreg[0][kc], dacc);
-        }
-        // The last sub-block issues phase C's first operands ahead of its
-        // softmax work.
-        if (sb == SUB - 1) read_c(0, 0);
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
-        const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
-        const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
-                              l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-        const int key = kw0 + 32 * sb + l32;
-        float pv[16], dsv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(sacc[i], c_scale, -lv[i]));
-          if constexpr (MASK) {
-            const int q = qt + c_item(i, hh);
-            const bool valid = key < Nk && (!CAUSAL || key <= q + off);
-            pr = valid ? pr : 0.0f;
-          }
-          pv[i] = pr;
-          dsv[i] = pr * dacc[i];
-        }
-        pP[sb][0] = pack8<T>(pv);
-        pP[sb][1] = pack8<T>(pv + 8);
-        pS[sb][0][0] = pack8<T>(dsv);
-        pS[sb][0][1] = pack8<T>(dsv + 8);
-        __builtin_amdgcn_sched_barrier(0);
+        s[sb] = (f32x16){};
       }
-    } else {
-      f32x16 s[SUB], dp[SUB];
-      {
-        // dP starts from -Dvec of its query so that the product yields dP - Dvec.
-        const f32x4 n0 = *reinterpret_cast<const f32x4*>(nd);
-        const f32x4 n1 = *reinterpret_cast<const f32x4*>(nd + 4);
-        const f32x4 n2 = *reinterpret_cast<const f32x4*>(nd + 16);
-        const f32x4 n3 = *reinterpret_cast<const f32x4*>(nd + 20);
+    }
+    // Phase A: S = Q K^T, dP = dO V^T over the 8 head_dim chunks.
+    u32x4 aq[2], ado[2], ak[2][SUB], av[2];
+    auto read_a = [&](int kc, int slot) {
+      aq[slot] = lds_ld16(qs, qo(kc));
+      ado[slot] = lds_ld16(dos, qo(kc));
 #pragma unroll
-        for (int sb = 0; sb < SUB; ++sb) {
-          dp[sb] = (f32x16){n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3],
-                            n2[0], n2[1], n2[2], n2[3], n3[0], n3[1], n3[2], n3[3]};
-          s[sb] = (f32x16){};
-        }
-      }
-      // Phase A: S = Q K^T, dP = dO V^T over the 8 head_dim chunks.
-      u32x4 aq[2], ado[2], ak[2][SUB], av[2];
-      auto read_a = [&](int kc, int slot) {
-        aq[slot] = lds_ld16(qs, q_off[kc]);
-        ado[slot] = lds_ld16(dos, q_off[kc]);
+      for (int sb = 0; sb < SUB; ++sb) ak[slot][sb] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, qo(kc));
+      av[slot] = lds_ld16(Vs + 32 * wave * D, qo(kc));
+    };
+    read_a(0, 0);
 #pragma unroll
-        for (int sb = 0; sb < SUB; ++sb) ak[slot][sb] = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);
-        av[slot] = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
-      };
-      read_a(0, 0);
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int cur = kc & 1;
-        if (kc + 1 < KC) read_a(kc + 1, cur ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int sb = 0; sb < SUB; ++sb) {
-          s[sb] = mfma32x32x16<T>(aq[cur], ak[cur][sb], s[sb]);
-          dp[sb] = mfma32x32x16<T>(ado[cur], sb == SUB - 1 ? av[cur] : vreg[0][kc], dp[sb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // Phase C's first operands and the LSE, issued ahead of the softmax.
-      read_c(0, 0);
-      const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
-      const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
-      const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
-      const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
-                            l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
-      // Phase B: P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded.
+    for (int kc = 0; kc < KC; ++kc) {
+      const int cur = kc & 1;
+      if (kc + 1 < KC) read_a(kc + 1, cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int sb = 0; sb < SUB; ++sb) {
-        const int key = kw0 + 32 * sb + l32;
-        float pv[16], dsv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c_scale, -lv[i]));
-          if constexpr (MASK) {
-            const int q = qt + c_item(i, hh);
-            const bool valid = key < Nk && (!CAUSAL || key <= q + off);
-            pr = valid ? pr : 0.0f;
-          }
-          pv[i] = pr;
-          dsv[i] = pr * dp[sb][i];
-        }
-        pP[sb][0] = pack8<T>(pv);
-        pP[sb][1] = pack8<T>(pv + 8);
-        pS[sb][0][0] = pack8<T>(dsv);
-        pS[sb][0][1] = pack8<T>(dsv + 8);
+        s[sb] = mfma32x32x16<T>(aq[cur], ak[cur][sb], s[sb]);
+        dp[sb] = mfma32x32x16<T>(ado[cur], sb == SUB - 1 ? av[cur] : vreg[0][kc], dp[sb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Phase C's first operands and the LSE, issued ahead of the softmax.
+    read_c(0, 0);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(ls + 4);
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(ls + 16);
+    const f32x4 l3 = *reinterpret_cast<const f32x4*>(ls + 20);
+    const float lv[16] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3],
+                          l2[0], l2[1], l2[2], l2[3], l3[0], l3[1], l3[2], l3[3]};
+    // Phase B: P = exp2(S*c - LSE*log2 e), dS = P o (dP - Dvec), rounded.
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int key = kw0 + 32 * sb + l32;
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c_scale, -lv[i]));
+        if constexpr (MASK) {
+          const int q = qt + c_item(i, hh);
+          const bool valid = key < Nk && (!CAUSAL || key <= q + off);
+          pr = valid ? pr : 0.0f;
+        }
+        pv[i] = pr;
+        dsv[i] = pr * dp[sb][i];
+      }
+      pP[sb][0] = pack8<T>(pv);
+      pP[sb][1] = pack8<T>(pv + 8);
+      pS[sb][0][0] = pack8<T>(dsv);
+      pS[sb][0][1] = pack8<T>(dsv + 8);
     }
     __builtin_amdgcn_sched_barrier(0);
     // Phase C: dV += P^T dO, dK += dS^T Q; step j = (16-row half c, d block db).
