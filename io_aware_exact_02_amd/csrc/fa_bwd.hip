@@ -210,12 +210,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // 0.619 -> 0.596, non-causal B2 H12 N2048 0.317 -> 0.280).
   constexpr bool VH = D == 128 && SUB == 2;
   constexpr int NST = VH ? 1 : 2;  // dS^T buffers
-  // PIPE: the software-pipelined VH loops (compute_vh, and the dQ loop), for
-  // causal launches.  Measured against the plain loops (in-process A/B on one
-  // box): causal B1 H8 N8192 backward 0.591 -> 0.561 ms, B1 H16 N8192 1.17
-  // -> 1.04 ms, B1 H2 N16384 0.571 -> 0.541 ms; non-causal B2 H12 N2048
-  // 0.273 -> 0.310 ms (its form spills more registers), so not there.
-  constexpr bool PIPE = CAUSAL;
+  // The VH form runs the software-pipelined loops (compute_vh, and the dQ
+  // loop).  Measured against the plain loops (in-process A/B on one box,
+  // backward ms): causal B1 H8 N8192 0.591 -> 0.561, B1 H16 N8192 1.17 ->
+  // 1.04, B1 H2 N16384 0.571 -> 0.541; non-causal, once the offsets of
+  // compute_vh stopped holding registers, B1 H8 N8192 1.033 -> 0.834 and
+  // B2 H12 N2048 0.278 -> 0.239 (before that it spilled and was slower).
   // PIPE64Q: the pipelined dQ loop at head_dim 64 too (in-process A/B,
   // backward ms: B1 H16 N16384 causal 1.601 -> 1.582, B2 H12 N2048
   // non-causal 0.098 -> 0.096, B1 H2 N16384 causal 0.240 -> 0.242).  The
@@ -493,8 +493,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // ---- S, dP, P, dS, dV, dK for this wave's 32*SUB keys and one query tile.
-  // The sub-blocks share each operand read from LDS.
+  // ---- S, dP, P, dS, dV, dK for this wave's 32*SUB keys and one query tile
+  // (the head_dim-64 shape; head_dim 128 runs compute_vh).  The sub-blocks
+  // share each operand read from LDS.
   auto compute = [&](auto bufc, auto maskc, int qt, u32x4 (&pS)[SUB][NQB][2]) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr bool MASK = decltype(maskc)::value;
@@ -532,17 +533,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
             kop = kreg[sb][kc];
           }
           s[sb] = mfma32x32x16<T>(aq, kop, s[sb]);
-          u32x4 vop;
-          if constexpr (VH) {
-            if (sb == SUB - 1) {
-              vop = lds_ld16(Vs + 32 * wave * D, q_off[kc]);
-            } else {
-              vop = vreg[sb < SUB - 1 ? sb : 0][kc];
-            }
-          } else {
-            vop = vreg[sb][kc];
-          }
-          dp[sb] = mfma32x32x16<T>(ado, vop, dp[sb]);
+          dp[sb] = mfma32x32x16<T>(ado, vreg[sb][kc], dp[sb]);
         }
       }
       const f32x4 l0 = *reinterpret_cast<const f32x4*>(ls + 32 * qb);
@@ -575,13 +566,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     // LLVM's MFMA interleaving strategy 1 for the rest of the tile: measured
     // 4-7% faster at head_dim 64, slower at 128.
     if constexpr (D == 64) __builtin_amdgcn_iglp_opt(1);
-    // Head_dim 128 (one wave per SIMD, the dK/dV accumulators of 64 keys in
-    // the 256 AGPRs): without this barrier the scheduler hoists the LDS reads
-    // of the dV/dK products above the softmax and runs out of registers
-    // (700-900 spilled VGPRs; 2-6 with it in the query-segment and
-    // non-causal forms).  Barriers inside the read loops as well (every 1, 2
-    // or 4 steps) measured within 1% of this alone.
-    if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
     // dV += P^T dO, dK += dS^T Q over the tile's query rows; each operand
     // read from LDS serves every sub-block.
 #pragma unroll
@@ -607,7 +591,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // ---- The VH form of the tile computation, software-pipelined: with one
   // wave per SIMD nothing else hides the LDS latency, so each loop issues
   // the operand reads of its next step (two register slots) before the
-  // MFMAs of the current one, and sched_barrier fixes that order.
+  // MFMAs of the current one, and sched_barrier fixes that order.  (The
+  // dK/dV accumulators of 64 keys fill the 256 AGPRs; left to itself the
+  // scheduler hoisted every operand read of the tile above the MFMAs and
+  // spilled 700-900 VGPRs.)
   auto compute_vh = [&](auto bufc, auto maskc, int qt, u32x4 (&pS)[SUB][NQB][2]) {
     static_assert(VH && NQB == 1 && KLDS, "head_dim 128, 32-row tiles");
     constexpr int BUF = decltype(bufc)::value;
@@ -730,7 +717,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       // under the mask too: its P and dS are exactly 0.
       const bool need_mask =
           (CAUSAL && kw0 + 32 * SUB - 1 > qt + off) || (kw0 + 32 * SUB - 1 >= Nk);
-      if constexpr (VH && PIPE) {
+      if constexpr (VH) {
         if (need_mask) {
           compute_vh(bufc, IntC<1>{}, qt, pS);
         } else {
@@ -767,7 +754,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
 
     // dQ(tile) = dS K over the workgroup's keys.
     const uint16_t* sts = dSt + (VH ? 0 : BUF * STILE);
-    if constexpr ((VH && PIPE) || (PIPE64Q && BPW == 1)) {
+    if constexpr (VH || (PIPE64Q && BPW == 1)) {
       // One 32x32 block per wave (or none), pipelined like compute_vh.
       static_assert(BPW == 1, "one dQ block per wave");
       f32x16 acc = (f32x16){};
