@@ -222,6 +222,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
   // pipelined dV/dK loop there was no better than LLVM's interleaving
   // (1.590 and 1.607 ms at B1 H16 N16384 with and without the dQ one).
   constexpr bool PIPE64Q = D == 64;
+  // PIPEC: the head_dim-64 query-segment form (narrow launches) pipelines
+  // its dV/dK loop too, which its registers allow once the offsets come from
+  // opaque per-tile bases (spills 9 -> 0).  In-process A/B, backward ms:
+  // causal B1 H2 N16384 0.246 -> 0.223; non-causal B2 H12 N512 and B2 H4
+  // N4096 unchanged (0.035, 0.112).  At c5 (unsegmented) it made no
+  // difference, so that form keeps LLVM's interleaving.
+  constexpr bool PIPEC = D == 64 && SEG;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[VH ? NW * 32 * D : 8];
@@ -504,6 +511,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     const float* ls = lse_s + BUF * BQ + 8 * hh;
     const float* nd = ndv_s + BUF * BQ + 8 * hh;
     u32x4 pP[SUB][NQB][2];
+    // PIPEC: LDS offsets formed from opaque per-tile bases (as in compute_vh)
+    // and the dV/dK loop pipelined instead of LLVM's interleaving.
+    uint32_t qo0 = q_off[0], qt0 = qt_off[0][0], qt1 = qt_off[1][0];
+    if constexpr (PIPEC) asm volatile("" : "+v"(qo0), "+v"(qt0), "+v"(qt1));
+    auto qo = [&](int kc) { return PIPEC ? qo0 ^ static_cast<uint32_t>(32 * kc) : q_off[kc]; };
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       // C value i: query qt + 32*qb + c_item(i, hh), key = this lane's key of
@@ -522,13 +534,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 aq = lds_ld16(qs + 32 * qb * D, q_off[kc]);
-        const u32x4 ado = lds_ld16(dos + 32 * qb * D, q_off[kc]);
+        const u32x4 aq = lds_ld16(qs + 32 * qb * D, qo(kc));
+        const u32x4 ado = lds_ld16(dos + 32 * qb * D, qo(kc));
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           u32x4 kop;
           if constexpr (KLDS) {
-            kop = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, q_off[kc]);  // this sub-block's keys
+            kop = lds_ld16(Ks + 32 * (SUB * wave + sb) * D, qo(kc));  // this sub-block's keys
           } else {
             kop = kreg[sb][kc];
           }
@@ -565,9 +577,36 @@ __global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(BwdParams p) {
     }
     // LLVM's MFMA interleaving strategy 1 for the rest of the tile: measured
     // 4-7% faster at head_dim 64, slower at 128.
-    if constexpr (D == 64) __builtin_amdgcn_iglp_opt(1);
+    if constexpr (D == 64 && !PIPEC) __builtin_amdgcn_iglp_opt(1);
     // dV += P^T dO, dK += dS^T Q over the tile's query rows; each operand
     // read from LDS serves every sub-block.
+    if constexpr (PIPEC) {
+      // Step j = (qb, c, db) issues the reads of step j+1 first.
+      constexpr int NJ = NQB * 2 * DB;
+      u32x4 bdo[2], bq[2];
+      auto read_c = [&](int j, int slot) {
+        const int qb = j / (2 * DB), c = (j / DB) % 2, db = j % DB;
+        const int r = 32 * qb + 16 * c;
+        const uint32_t x = static_cast<uint32_t>(64 * db);
+        bdo[slot] = lds_tr16(dos + r * D, qt0 ^ x, qt1 ^ x);
+        bq[slot] = lds_tr16(qs + r * D, qt0 ^ x, qt1 ^ x);
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      read_c(0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int qb = j / (2 * DB), c = (j / DB) % 2, db = j % DB, cur = j & 1;
+        if (j + 1 < NJ) read_c(j + 1, cur ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          dvacc[sb][db] = mfma32x32x16<T>(pP[sb][qb][c], bdo[cur], dvacc[sb][db]);
+          dkacc[sb][db] = mfma32x32x16<T>(pS[sb][qb][c], bq[cur], dkacc[sb][db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
